@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused fp32 convolution hot path on one MI355X.
+
+One step = one call of each entry point on its full-size workload, in this order:
+  conv3d_div_maxpool_gap_bias_sum  x [128,8,16,64,64]      -> out [128]
+  conv3d_mish_tanh                 x [16,32,32,64,64]      -> y [16,64,30,62,62]
+  dwsep_conv2d                     x [16,64,512,512]       -> y [16,128,512,512]
+  dwsep_conv2d (odd, biased)       x [8,96,333,517]        -> y [8,192,333,517]
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+`value` is the step's convolution work (2 x multiply-adds) per second, in TFLOP/s.
+Each launch is also timed with HIP events on the stream it runs on; the per-workload
+numbers, the roofline fraction of the dominant kernel and a CPU-oracle baseline on a
+bounded sample are printed on the same JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+BENCH_WORKLOADS = (2, 3, 4, 5)
+
+
+def work(w):
+    """Algorithmic multiply-adds and bytes (inputs + weights + outputs, each once)."""
+    d, p = w.dims, w.params
+    if w.op == "conv3d_mish_tanh":
+        k = p["k"]
+        od, oh, ow = (d[s] - k + 1 for s in ("D", "H", "W"))
+        outs = d["N"] * d["O"] * od * oh * ow
+        macs = outs * d["C"] * k ** 3
+        nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
+                      + d["O"] + outs)
+    elif w.op == "conv3d_div_maxpool_gap_bias_sum":
+        k = p["k"]
+        od, oh, ow = (d[s] - k + 1 for s in ("D", "H", "W"))
+        macs = d["N"] * d["O"] * od * oh * ow * d["C"] * k ** 3
+        nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
+                      + 2 * d["O"] + d["N"])
+    else:
+        K = p["K"]
+        pix = d["N"] * d["H"] * d["W"]   # stride 1, "same" padding: Ho = H, Wo = W
+        macs = pix * d["C"] * K * K + pix * d["O"] * d["C"]
+        nbytes = 4 * (pix * d["C"] + d["C"] * K * K + d["O"] * d["C"] + pix * d["O"]
+                      + (d["C"] + d["O"] if p["bias"] else 0))
+    return macs, nbytes
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = ROOT / "implicit_gemm_convolution_conv3d_amd" / "csrc"
+    for f in sorted(csrc.glob("*")):
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only if it was
+    taken on the current kernel sources."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    try:
+        data = json.loads(f.read_text())
+    except ValueError:
+        return None
+    ent = data.get(kernel_name)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def run_op(cf, w, t, out):
+    p = w.params
+    if w.op == "conv3d_mish_tanh":
+        cf.conv3d_mish_tanh(t["x"], t["w"], t["b"], p["stride"], p["pad"], out=out)
+    elif w.op == "conv3d_div_maxpool_gap_bias_sum":
+        cf.conv3d_div_maxpool_gap_bias_sum(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"],
+                                           t["bias"], out=out)
+    else:
+        cf.dwsep_conv2d(t["x"], t["dw_w"], t["dw_b"], t["pw_w"], t["pw_b"], p["stride"],
+                        p["pad"], p["dilation"], out=out)
+
+
+def out_shape(w):
+    d, p = w.dims, w.params
+    if w.op == "conv3d_mish_tanh":
+        k = p["k"]
+        return (d["N"], d["O"], d["D"] - k + 1, d["H"] - k + 1, d["W"] - k + 1)
+    if w.op == "conv3d_div_maxpool_gap_bias_sum":
+        return (d["N"],)
+    return (d["N"], d["O"], d["H"], d["W"])
+
+
+def cpu_baseline(workloads, frac_batch):
+    """The fp64 oracle, untouched, on the first batch items of each workload.  Input
+    generation is outside the timed region.  Returns (TFLOP/s, threads, description)."""
+    import oracle
+    total_macs, secs, parts = 0, 0.0, []
+    for w in workloads:
+        d, p = w.dims, w.params
+        nb = max(1, int(round(d["N"] * frac_batch)))
+        inp = w.inputs()
+        x = np.ascontiguousarray(inp["x"][:nb])
+        macs, _ = work(w)
+        t0 = time.perf_counter()
+        if w.op == "conv3d_mish_tanh":
+            oracle.conv3d_mish_tanh(x, inp["w"], inp["b"], p["stride"], p["pad"])
+        elif w.op == "conv3d_div_maxpool_gap_bias_sum":
+            oracle.conv3d_div_maxpool_gap_bias_sum(x, inp["w"], inp["conv_b"], p["divisor"],
+                                                   p["pool"], inp["bias"])
+        else:
+            oracle.dwsep_conv2d(x, inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
+                                p["stride"], p["pad"], p["dilation"])
+        secs += time.perf_counter() - t0
+        total_macs += macs * nb // d["N"]
+        parts.append("%s batch items 0..%d of %d" % (w.name, nb - 1, d["N"]))
+        del inp, x
+    desc = "; ".join(parts) + " (%.1f s of fp64 naive loops)" % secs
+    return 2 * total_macs / secs / 1e12, oracle.threads(), desc
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-frac", type=float, default=0.125,
+                    help="fraction of each workload's batch the oracle baseline runs on")
+    ap.add_argument("--workloads", default=",".join(map(str, BENCH_WORKLOADS)))
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(batch sharding needs no communication; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import implicit_gemm_convolution_conv3d_amd as cf
+    from implicit_gemm_convolution_conv3d_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cf.lib()  # fail loudly now if the library is missing
+    dev = torch.device("cuda:0")
+    ids = [int(s) for s in args.workloads.split(",") if s]
+    wls = [wl.WORKLOADS[i] for i in ids]
+
+    tensors, outs = [], []
+    for w in wls:
+        inp = w.inputs()
+        tensors.append({k: (None if v is None else torch.from_numpy(v).to(dev))
+                        for k, v in inp.items()})
+        outs.append(torch.empty(out_shape(w), dtype=torch.float32, device=dev))
+        del inp
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for w, t, o in zip(wls, tensors, outs):
+            run_op(cf, w, t, o)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in wls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (w, t, o) in enumerate(zip(wls, tensors, outs)):
+            ev[s][i][0].record(stream)
+            run_op(cf, w, t, o)
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per = {}
+    step_macs = 0
+    dominant, dom_ms = None, -1.0
+    for i, w in enumerate(wls):
+        times = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
+        macs, nbytes = work(w)
+        step_macs += macs
+        avg = float(times.mean())
+        tfl = 2 * macs / (avg * 1e-3) / 1e12
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        per[w.name] = {
+            "op": w.op, "ms_avg": round(avg, 4), "ms_min": round(float(times.min()), 4),
+            "tflops": round(tfl, 2), "frac_fp32_mfma": round(tfl / PEAK_FP32_TFLOPS, 4),
+            "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "gflop": round(2 * macs / 1e9, 3), "mbytes": round(nbytes / 1e6, 2),
+        }
+        if avg > dom_ms:
+            dominant, dom_ms = w, avg
+    value = 2 * step_macs / (ms_per_step * 1e-3) / 1e12
+
+    dmacs, dbytes = work(dominant)
+    kname = {"conv3d_mish_tanh": "conv3d_mish_tanh_kernel",
+             "conv3d_div_maxpool_gap_bias_sum": "conv3d_pool_sum_kernel",
+             "dwsep_conv2d": "dwsep_kernel"}[dominant.op]
+    achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                "traffic": load_traffic(dominant.name), "kernel": kname,
+                "workload": dominant.name}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del tensors, outs
+        torch.cuda.empty_cache()
+        v, cores, desc = cpu_baseline(wls, args.cpu_sample_frac)
+        cpu = {"value": round(v, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": desc}
+
+    line = {
+        "metric": "conv TFLOP/s (2xMACs) and % fp32 MFMA/HBM roofline per config, 1xMI355X",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fused conv hot path: " + " + ".join(w.name for w in wls),
+                   "per_workload": per, "kernel_source_sha": kernel_source_sha()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

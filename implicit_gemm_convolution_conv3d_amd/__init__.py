@@ -1,0 +1,162 @@
+"""Fused fp32 convolutions for AMD MI355X (gfx950): a thin ctypes binding over
+``libconvfuse.so``.
+
+The binding only marshals arguments: it checks that tensors are contiguous fp32 on the
+current GPU, allocates outputs with torch, and passes raw device pointers and the current
+HIP stream to the C ABI declared in ``include/convfuse.h``.  Every arithmetic step runs in
+the library's HIP kernels; there is no fallback path, and a missing or unloadable library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import threading
+
+from . import _build
+
+__all__ = [
+    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d", "conv_out_len",
+    "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
+]
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_DEVICE = 0, 1, 2, 3, 4
+_ERR_NAMES = {ERR_NULL: "NULL", ERR_SHAPE: "SHAPE", ERR_UNSUPPORTED: "UNSUPPORTED",
+              ERR_DEVICE: "DEVICE"}
+
+EXPORTED_SYMBOLS = (
+    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d",
+    "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
+)
+
+_lib = None
+_lock = threading.Lock()
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class ConvFuseError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__("convfuse error %s (%d): %s" % (_ERR_NAMES.get(code, "?"), code, message))
+        self.code = code
+
+
+def library_path():
+    return _build.LIB
+
+
+def lib():
+    """The loaded libconvfuse.so (built in-tree first if it does not exist yet)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not _build.LIB.exists():
+                _build.build()
+            L = ctypes.CDLL(str(_build.LIB))
+            L.conv3d_mish_tanh.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
+            L.conv3d_div_maxpool_gap_bias_sum.argtypes = (
+                [_vp] * 3 + [ctypes.c_float, _i64, _vp, _vp] + [_i64] * 7 + [_vp])
+            L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
+            L.convfuse_conv_out_len.argtypes = [_i64] * 5 + [ctypes.POINTER(_i64)]
+            L.convfuse_last_error.restype = ctypes.c_char_p
+            L.convfuse_abi_version.restype = ctypes.c_int
+            for name in ("conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d",
+                         "convfuse_conv_out_len"):
+                getattr(L, name).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise ConvFuseError(rc, lib().convfuse_last_error().decode(errors="replace"))
+
+
+def conv_out_len(n, k, stride=1, pad=0, dilation=1):
+    out = _i64()
+    _check(lib().convfuse_conv_out_len(n, k, stride, pad, dilation, ctypes.byref(out)))
+    return out.value
+
+
+def _ptr(t, name, shape=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32 (got %s)" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t.data_ptr() or None
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None):
+    """y = tanh(mish(conv3d(x, w) + b)); x [N,Cin,D,H,W], w [Cout,Cin,k,k,k], b [Cout]."""
+    import torch
+    N, C, D, H, W = x.shape
+    O, C2, k = w.shape[0], w.shape[1], w.shape[2]
+    if C2 != C or tuple(w.shape[2:]) != (k, k, k):
+        raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
+    if b is not None and tuple(b.shape) != (O,):
+        raise ValueError("bias must have shape (%d,)" % O)
+    shp = (N, O) + tuple(conv_out_len(s, k, stride, padding) for s in (D, H, W))
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().conv3d_mish_tanh(_ptr(x, "x"), _ptr(w, "w"), _ptr(b, "b"),
+                                      _ptr(out, "out", shp), N, C, D, H, W, O, k, stride,
+                                      padding, _stream(x)))
+    return out
+
+
+def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out=None):
+    """out[n] = sum_c(mean(maxpool((conv3d(x,w)+conv_b)/divisor)) + bias[c]); out [N]."""
+    import torch
+    N, C, D, H, W = x.shape
+    O, C2, k = w.shape[0], w.shape[1], w.shape[2]
+    if C2 != C or tuple(w.shape[2:]) != (k, k, k):
+        raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
+    if conv_b is not None and tuple(conv_b.shape) != (O,):
+        raise ValueError("conv_b must have shape (%d,)" % O)
+    if bias.numel() != O:
+        raise ValueError("bias must have %d elements" % O)
+    if out is None:
+        out = torch.empty((N,), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().conv3d_div_maxpool_gap_bias_sum(
+            _ptr(x, "x"), _ptr(w, "w"), _ptr(conv_b, "conv_b"), float(divisor), pool,
+            _ptr(bias, "bias"), _ptr(out, "out", (N,)), N, C, D, H, W, O, k, _stream(x)))
+    return out
+
+
+def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out=None):
+    """y = pointwise(depthwise(x)); x [N,Cin,H,W], dw_w [Cin,1,K,K], pw_w [Cout,Cin,1,1]."""
+    import torch
+    N, C, H, W = x.shape
+    K = dw_w.shape[-1]
+    O = pw_w.shape[0]
+    if tuple(dw_w.shape) != (C, 1, K, K) or tuple(pw_w.shape) != (O, C, 1, 1):
+        raise ValueError("weights %s / %s do not match input %s"
+                         % (tuple(dw_w.shape), tuple(pw_w.shape), tuple(x.shape)))
+    if dw_b is not None and tuple(dw_b.shape) != (C,):
+        raise ValueError("dw_b must have shape (%d,)" % C)
+    if pw_b is not None and tuple(pw_b.shape) != (O,):
+        raise ValueError("pw_b must have shape (%d,)" % O)
+    shp = (N, O, conv_out_len(H, K, stride, padding, dilation),
+           conv_out_len(W, K, stride, padding, dilation))
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().dwsep_conv2d(_ptr(x, "x"), _ptr(dw_w, "dw_w"), _ptr(dw_b, "dw_b"),
+                                  _ptr(pw_w, "pw_w"), _ptr(pw_b, "pw_b"), _ptr(out, "out", shp),
+                                  N, C, H, W, O, K, stride, padding, dilation, _stream(x)))
+    return out

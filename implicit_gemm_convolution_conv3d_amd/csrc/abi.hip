@@ -1,0 +1,179 @@
+// abi.hip -- the extern "C" entry points of libconvfuse.so: argument validation, output
+// shapes, and dispatch to the gfx950 kernels on the caller's stream.  Every check runs
+// before anything is launched; no entry point allocates memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/convfuse.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+// Largest size accepted for one dimension or channel count: keeps every in-kernel
+// 32-bit local index and the per-dimension arithmetic far from overflow.
+constexpr int64_t kMaxDim = 1LL << 24;
+// Largest element count of one tensor: byte offsets stay below 2^62.
+constexpr int64_t kMaxElems = 1LL << 60;
+
+bool out_len(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d, int64_t *out)
+{
+    if (in <= 0 || k <= 0 || s <= 0 || p < 0 || d <= 0) return false;
+    if (in > kMaxDim || k > kMaxDim || p > kMaxDim || d > kMaxDim) return false;
+    const int64_t span = in + 2 * p - d * (k - 1) - 1;
+    if (span < 0) return false;
+    *out = span / s + 1;
+    return true;
+}
+
+bool elems_ok(std::initializer_list<int64_t> dims)
+{
+    int64_t total = 1;
+    for (int64_t v : dims) {
+        if (v < 0 || v > kMaxDim * 64) return false;
+        if (v != 0 && total > kMaxElems / v) return false;
+        total *= v;
+    }
+    return true;
+}
+
+int device_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return CONVFUSE_OK;
+    return fail(CONVFUSE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int convfuse_abi_version(void) { return 100; }
+
+const char *convfuse_last_error(void) { return g_err; }
+
+int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dilation,
+                          int64_t *out)
+{
+    if (!out) return fail(CONVFUSE_ERR_NULL, "convfuse_conv_out_len: out is NULL");
+    int64_t v;
+    if (!out_len(in, k, stride, pad, dilation, &v) || v <= 0)
+        return fail(CONVFUSE_ERR_SHAPE,
+                    "convfuse_conv_out_len: in=%lld k=%lld stride=%lld pad=%lld dilation=%lld "
+                    "gives no output",
+                    (long long)in, (long long)k, (long long)stride, (long long)pad,
+                    (long long)dilation);
+    *out = v;
+    return CONVFUSE_OK;
+}
+
+int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y, int64_t N,
+                     int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout, int64_t k,
+                     int64_t stride, int64_t pad, void *stream)
+{
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "conv3d_mish_tanh: bad N=%lld Cin=%lld Cout=%lld",
+                    (long long)N, (long long)Cin, (long long)Cout);
+    int64_t OD, OH, OW;
+    if (!out_len(D, k, stride, pad, 1, &OD) || !out_len(H, k, stride, pad, 1, &OH) ||
+        !out_len(W, k, stride, pad, 1, &OW) || OD <= 0 || OH <= 0 || OW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE,
+                    "conv3d_mish_tanh: D=%lld H=%lld W=%lld k=%lld stride=%lld pad=%lld give no "
+                    "output",
+                    (long long)D, (long long)H, (long long)W, (long long)k, (long long)stride,
+                    (long long)pad);
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}))
+        return fail(CONVFUSE_ERR_SHAPE, "conv3d_mish_tanh: tensor too large");
+    if (k != 3 || stride != 1 || pad > 2)
+        return fail(CONVFUSE_ERR_UNSUPPORTED,
+                    "conv3d_mish_tanh: GPU path implements k=3, stride=1, pad<=2 (got k=%lld "
+                    "stride=%lld pad=%lld)",
+                    (long long)k, (long long)stride, (long long)pad);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "conv3d_mish_tanh: x, w and y are required");
+    convfuse::Conv3dDims d{N, Cin, D, H, W, Cout, OD, OH, OW, (int)pad};
+    return device_status(convfuse::launch_conv3d_mish_tanh(x, w, b, y, d, (hipStream_t)stream),
+                         "conv3d_mish_tanh launch");
+}
+
+int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
+                                    float divisor, int64_t pool, const float *bias, float *out,
+                                    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                    int64_t Cout, int64_t k, void *stream)
+{
+    const char *fn = "conv3d_div_maxpool_gap_bias_sum";
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
+                    (long long)Cin, (long long)Cout);
+    if (!std::isfinite(divisor) || divisor == 0.0f)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: divisor must be finite and non-zero", fn);
+    int64_t OD, OH, OW, PD, PH, PW;
+    if (!out_len(D, k, 1, 0, 1, &OD) || !out_len(H, k, 1, 0, 1, &OH) ||
+        !out_len(W, k, 1, 0, 1, &OW) || OD <= 0 || OH <= 0 || OW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: D=%lld H=%lld W=%lld k=%lld give no conv output", fn,
+                    (long long)D, (long long)H, (long long)W, (long long)k);
+    if (!out_len(OD, pool, pool, 0, 1, &PD) || !out_len(OH, pool, pool, 0, 1, &PH) ||
+        !out_len(OW, pool, pool, 0, 1, &PW) || PD <= 0 || PH <= 0 || PW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: pool=%lld does not fit the %lldx%lldx%lld conv output",
+                    fn, (long long)pool, (long long)OD, (long long)OH, (long long)OW);
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (k != 3 || pool != 2)
+        return fail(CONVFUSE_ERR_UNSUPPORTED,
+                    "%s: GPU path implements k=3, pool=2 (got k=%lld pool=%lld)", fn,
+                    (long long)k, (long long)pool);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !w || !bias || !out)
+        return fail(CONVFUSE_ERR_NULL, "%s: x, w, bias and out are required", fn);
+    convfuse::PoolDims p{{N, Cin, D, H, W, Cout, OD, OH, OW, 0}, PD, PH, PW, divisor};
+    return device_status(
+        convfuse::launch_conv3d_pool_sum(x, w, conv_b, bias, out, p, (hipStream_t)stream),
+        "conv3d_div_maxpool_gap_bias_sum launch");
+}
+
+int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                 const float *pw_b, float *y, int64_t N, int64_t Cin, int64_t H, int64_t W,
+                 int64_t Cout, int64_t K, int64_t stride, int64_t pad, int64_t dilation,
+                 void *stream)
+{
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "dwsep_conv2d: bad N=%lld Cin=%lld Cout=%lld",
+                    (long long)N, (long long)Cin, (long long)Cout);
+    int64_t Ho, Wo;
+    if (!out_len(H, K, stride, pad, dilation, &Ho) || !out_len(W, K, stride, pad, dilation, &Wo) ||
+        Ho <= 0 || Wo <= 0)
+        return fail(CONVFUSE_ERR_SHAPE,
+                    "dwsep_conv2d: H=%lld W=%lld K=%lld stride=%lld pad=%lld dilation=%lld give "
+                    "no output",
+                    (long long)H, (long long)W, (long long)K, (long long)stride, (long long)pad,
+                    (long long)dilation);
+    if (!elems_ok({N, Cin, H, W}) || !elems_ok({N, Cout, Ho, Wo}))
+        return fail(CONVFUSE_ERR_SHAPE, "dwsep_conv2d: tensor too large");
+    if (K != 3 || stride != 1 || dilation != 1 || pad > 2)
+        return fail(CONVFUSE_ERR_UNSUPPORTED,
+                    "dwsep_conv2d: GPU path implements K=3, stride=1, dilation=1, pad<=2 (got "
+                    "K=%lld stride=%lld pad=%lld dilation=%lld)",
+                    (long long)K, (long long)stride, (long long)pad, (long long)dilation);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !dw_w || !pw_w || !y)
+        return fail(CONVFUSE_ERR_NULL, "dwsep_conv2d: x, dw_w, pw_w and y are required");
+    convfuse::DwsepDims d{N, Cin, H, W, Cout, Ho, Wo, (int)pad};
+    return device_status(
+        convfuse::launch_dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, y, d, (hipStream_t)stream),
+        "dwsep_conv2d launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// conv3d_igemm.hip -- implicit-GEMM Conv3d (k = 3, stride 1) on gfx950 fp32 matrix cores,
+// with two fused epilogues:
+//   * Mish then tanh, stored to y           (page "Kimi-K2.6 l2_p47", Conv3d + Mish + Tanh)
+//   * /divisor, 2x2x2 max-pool, global mean, reduced to one scalar per batch item with one
+//     atomic per workgroup                  (page "Kimi-K2.6 l2_p8", the rewrite of the
+//                                            output as a sum of channel means plus sum(bias))
+//
+// GEMM view (page l2_p47, implicit-GEMM paragraph): rows = output channels, columns =
+// output voxels, reduction K = Cin * 27 ordered tap-major, channel-minor.  One k-step of
+// the 16x16x4 MFMA consumes four consecutive input channels at one tap, so the B operand
+// of lane l is the LDS halo value of channel (l/16) at voxel column (l%16) shifted by the
+// tap: its LDS address is a per-lane base plus a compile-time offset.
+//
+// Workgroup = WD x WH waves.  Each wave owns a box of output voxels and all 16*MB output
+// channels of its channel group; the input halo of the workgroup's box is staged into
+// LDS one chunk of CC input channels at a time, together with the chunk's weights laid
+// out in MFMA fragment order ([tap][channel group][lane][MB]).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace convfuse {
+
+namespace {
+
+// tanh(mish(v)), mish(v) = v * tanh(softplus(v)), softplus(v) = v for v > 20 (PyTorch's
+// threshold).  For v <= 20, tanh(log(1 + e^v)) = n / (n + 2) with n = e^v (e^v + 2): one
+// exponential and one division instead of exp, log and tanh.  For v > 20, tanh(v) rounds
+// to 1 in fp32, so mish(v) = v.
+__device__ __forceinline__ float mish_tanh(float v)
+{
+    float t = 1.0f;
+    if (v <= 20.0f) {
+        float e = __expf(v);
+        float n = e * (e + 2.0f);
+        t = n / (n + 2.0f);
+    }
+    return tanhf(v * t);
+}
+
+// Copy one chunk of CC input channels of the halo box [id0, id0+HD) x [ih0, ih0+HH) x
+// [iw0, iw0+HW) into LDS (channel stride CS, row stride RS).  Out-of-range voxels and
+// channels >= C read as zero (zero padding, and the zero-weight tail of the last chunk).
+template <int CC, int HD, int HH, int HW, int RS, int CS, int NT>
+__device__ __forceinline__ void stage_halo(float *__restrict__ xs, const float *__restrict__ x,
+                                           const Conv3dDims &d, int64_t n, int c0, int id0,
+                                           int ih0, int iw0)
+{
+    constexpr int total = CC * HD * HH * HW;
+    for (int e = threadIdx.x; e < total; e += NT) {
+        const int col = e % HW;
+        const int row = e / HW;
+        const int hh = row % HH;
+        const int t = row / HH;
+        const int hd = t % HD;
+        const int c = t / HD;
+        const int ci = c0 + c, id = id0 + hd, ih = ih0 + hh, iw = iw0 + col;
+        float v = 0.0f;
+        if (ci < d.C && (unsigned)id < (unsigned)d.D && (unsigned)ih < (unsigned)d.H &&
+            (unsigned)iw < (unsigned)d.W)
+            v = x[(((n * d.C + ci) * d.D + id) * d.H + ih) * d.W + iw];
+        xs[c * CS + (hd * HH + hh) * RS + col] = v;
+    }
+}
+
+// Weights of output channels [o0, o0 + 16*MB) and input channels [c0, c0 + CC), written in
+// A-fragment order: ws[((tap * CC/4 + cg) * 64 + lane) * MB + mb] holds
+// w[o0 + 16*mb + lane%16][c0 + 4*cg + lane/16][tap].  Missing channels are zero.
+template <int CC, int MB, int NT>
+__device__ __forceinline__ void stage_weights(float *__restrict__ ws, const float *__restrict__ w,
+                                              const Conv3dDims &d, int o0, int c0)
+{
+    constexpr int total = MB * 16 * CC * 27;
+    for (int e = threadIdx.x; e < total; e += NT) {
+        const int tap = e % 27;
+        const int t = e / 27;
+        const int cl = t % CC;
+        const int ol = t / CC;
+        const int o = o0 + ol, c = c0 + cl;
+        float v = 0.0f;
+        if (o < d.O && c < d.C) v = w[((int64_t)o * d.C + c) * 27 + tap];
+        const int lane = (cl & 3) * 16 + (ol & 15);
+        ws[((tap * (CC / 4) + (cl >> 2)) * 64 + lane) * MB + (ol >> 4)] = v;
+    }
+}
+
+template <int MB>
+__device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
+{
+    if constexpr (MB % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < MB / 4; ++i) {
+            floatx4 v = *reinterpret_cast<const floatx4 *>(p + 4 * i);
+            a[4 * i + 0] = v[0];
+            a[4 * i + 1] = v[1];
+            a[4 * i + 2] = v[2];
+            a[4 * i + 3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) a[i] = p[i];
+    }
+}
+
+// The K loop shared by both epilogues.  Wave-local voxel blocks are given by NB block
+// offsets (in LDS floats, relative to the lane base); acc[mb][nb] accumulates output
+// channels 16*mb.. of block nb.
+template <int MB, int NB, int CC, int HH, int RS, int CS>
+__device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
+                                            const float *__restrict__ ws, int xlane,
+                                            const int (&boff)[NB], floatx4 (&acc)[MB][NB])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                for (int cg = 0; cg < CC / 4; ++cg) {
+                    const int tap = (kd * 3 + kh) * 3 + kw;
+                    float a[MB];
+                    load_afrag<MB>(ws + ((tap * (CC / 4) + cg) * 64 + lane) * MB, a);
+                    const int toff = cg * 4 * CS + (kd * HH + kh) * RS + kw;
+                    float bv[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bv[nb] = xs[xlane + toff + boff[nb]];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[mb][nb] = mfma_16x16x4(a[mb], bv[nb], acc[mb][nb]);
+                }
+}
+
+// ------------------------------------------------------------------ Mish/tanh epilogue
+// Wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns [ow0, ow0 + 16*NBW).
+template <int MB, int NBW, int WD, int WH, int CC>
+__global__ __launch_bounds__(64 * WD * WH) void conv3d_mish_tanh_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
+    float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
+{
+    constexpr int NT = 64 * WD * WH;
+    constexpr int HD = WD + 2, HH = WH + 2, HW = 16 * NBW + 2;
+    constexpr int RS = round_up(HW, 4);
+    constexpr int CS = halo_channel_stride(HD * HH * RS);
+    constexpr int XS = CC * CS;
+    constexpr int WSZ = 27 * CC * 16 * MB;
+    __shared__ __attribute__((aligned(16))) float lds[XS + WSZ];
+    float *xs = lds;
+    float *ws = lds + XS;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w); t /= tiles_w;
+    const int th = (int)(t % tiles_h); t /= tiles_h;
+    const int td = (int)(t % tiles_d); t /= tiles_d;
+    const int64_t n = t % d.N;
+    const int og = (int)(t / d.N);
+
+    const int od0 = td * WD, oh0 = th * WH, ow0 = tw * 16 * NBW, o0 = og * 16 * MB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wd = wave / WH, wh = wave % WH;
+    const int xlane = (lane >> 4) * CS + (wd * HH + wh) * RS + (lane & 15);
+    int boff[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) boff[nb] = 16 * nb;
+
+    floatx4 acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int od = od0 + wd, oh = oh0 + wh;
+    const bool active = od < d.OD && oh < d.OH;
+    for (int c0 = 0; c0 < d.C; c0 += CC) {
+        __syncthreads();
+        stage_halo<CC, HD, HH, HW, RS, CS, NT>(xs, x, d, n, c0, od0 - d.pad, oh0 - d.pad,
+                                               ow0 - d.pad);
+        stage_weights<CC, MB, NT>(ws, w, d, o0, c0);
+        __syncthreads();
+        if (active) igemm_chunk<MB, NBW, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
+    }
+    if (!active) return;
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+            if (o >= d.O) continue;
+            const float bias = b ? b[o] : 0.0f;
+            float *yrow = y + (((n * d.O + o) * d.OD + od) * d.OH + oh) * d.OW;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int ow = ow0 + 16 * nb + (lane & 15);
+                if (ow < d.OW) yrow[ow] = mish_tanh(acc[mb][nb][r] + bias);
+            }
+        }
+}
+
+// ------------------------------------------------------------------ pool/sum epilogue
+// Wave (wd, wh) owns pooled windows (pd0 + wd, ph0 + wh, [pw0, pw0 + 8*NBW)).  Its 4*NBW
+// voxel blocks are (dd, dh, q): conv voxel (2pd + dd, 2ph + dh, 2pw0 + 16q + j) for lane
+// column j, so the max over (dd, dh) is taken inside a lane and the max over the window's
+// two columns between lanes j and j^1.
+template <int MB, int NBW, int WD, int WH, int CC>
+__global__ __launch_bounds__(64 * WD * WH) void conv3d_pool_sum_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
+    float *__restrict__ out, PoolDims pd_, int64_t tiles, int tiles_w, int tiles_h,
+    int tiles_d, float inv_count)
+{
+    constexpr int NT = 64 * WD * WH;
+    constexpr int NB = 4 * NBW;
+    constexpr int HD = 2 * WD + 2, HH = 2 * WH + 2, HW = 16 * NBW + 2;
+    constexpr int RS = round_up(HW, 4);
+    constexpr int CS = halo_channel_stride(HD * HH * RS);
+    constexpr int XS = CC * CS;
+    constexpr int WSZ = 27 * CC * 16 * MB;
+    __shared__ __attribute__((aligned(16))) float lds[XS + WSZ];
+    __shared__ float red[NT / 64];
+    float *xs = lds;
+    float *ws = lds + XS;
+    const Conv3dDims &d = pd_.conv;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w); t /= tiles_w;
+    const int th = (int)(t % tiles_h); t /= tiles_h;
+    const int td = (int)(t % tiles_d); t /= tiles_d;
+    const int64_t n = t % d.N;
+    const int og = (int)(t / d.N);
+
+    const int pd0 = td * WD, ph0 = th * WH, pw0 = tw * 8 * NBW, o0 = og * 16 * MB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wd = wave / WH, wh = wave % WH;
+    const int xlane = (lane >> 4) * CS + (2 * wd * HH + 2 * wh) * RS + (lane & 15);
+    int boff[NB];
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) boff[(dd * 2 + dh) * NBW + q] = (dd * HH + dh) * RS + 16 * q;
+
+    floatx4 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int pdi = pd0 + wd, phi = ph0 + wh;
+    const bool active = pdi < pd_.PD && phi < pd_.PH;
+    for (int c0 = 0; c0 < d.C; c0 += CC) {
+        __syncthreads();
+        stage_halo<CC, HD, HH, HW, RS, CS, NT>(xs, x, d, n, c0, 2 * pd0, 2 * ph0, 2 * pw0);
+        stage_weights<CC, MB, NT>(ws, w, d, o0, c0);
+        __syncthreads();
+        if (active) igemm_chunk<MB, NB, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
+    }
+
+    // (conv + cb) / divisor is monotone in conv: increasing for a positive divisor, so the
+    // window maximum of the divided values is (max conv + cb) / divisor; for a negative
+    // divisor it is (min conv + cb) / divisor.
+    const bool use_min = pd_.divisor < 0.0f;
+    const int j = lane & 15;
+    float part = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+            const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < NBW; ++q) {
+                float m = acc[mb][q][r];
+#pragma unroll
+                for (int p = 1; p < 4; ++p) {
+                    const float v = acc[mb][p * NBW + q][r];
+                    m = use_min ? fminf(m, v) : fmaxf(m, v);
+                }
+                const float m2 = __shfl_xor(m, 1, 64);
+                m = use_min ? fminf(m, m2) : fmaxf(m, m2);
+                const int pw = pw0 + 8 * q + (j >> 1);
+                if (active && o < d.O && (j & 1) == 0 && pw < pd_.PW)
+                    part += (m + cbv) / pd_.divisor;
+            }
+        }
+    part = wave_sum(part);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) s += red[i];
+        atomicAdd(out + n, s * inv_count);
+    }
+}
+
+// out[n] = sum_c bias[c]: the constant part of the page-l2_p8 rewrite, written before the
+// pooled partial sums are added.
+__global__ void pool_sum_init_kernel(const float *__restrict__ bias, float *__restrict__ out,
+                                     int64_t N, int64_t O)
+{
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float s = 0.0f;
+    for (int64_t c = 0; c < O; ++c) s += bias[c];
+    out[n] = s;
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <int MB, int NBW, int WD, int WH, int CC>
+hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
+                      const Conv3dDims &d, hipStream_t s)
+{
+    const int64_t tw = cdiv(d.OW, 16 * NBW), th = cdiv(d.OH, WH), td = cdiv(d.OD, WD);
+    const int64_t og = cdiv(d.O, 16 * MB);
+    const int64_t tiles = tw * th * td * d.N * og;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC>), dim3((unsigned)tiles),
+                       dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles, (int)tw, (int)th, (int)td);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
+                                   const Conv3dDims &d, hipStream_t s)
+{
+    const bool wide = d.OW > 16;
+    if (d.O > 16) {
+        if (wide) return launch_act<4, 4, 2, 2, 4>(x, w, b, y, d, s);
+        return launch_act<4, 1, 2, 2, 4>(x, w, b, y, d, s);
+    }
+    if (wide) return launch_act<1, 4, 2, 2, 4>(x, w, b, y, d, s);
+    return launch_act<1, 1, 2, 2, 4>(x, w, b, y, d, s);
+}
+
+hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *conv_b,
+                                  const float *bias, float *out, const PoolDims &p,
+                                  hipStream_t s)
+{
+    constexpr int MB = 1, NBW = 4, WD = 1, WH = 4, CC = 4;
+    const Conv3dDims &d = p.conv;
+    hipLaunchKernelGGL(pool_sum_init_kernel, dim3((unsigned)cdiv(d.N, 256)), dim3(256), 0, s,
+                       bias, out, d.N, d.O);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t tw = cdiv(p.PW, 8 * NBW), th = cdiv(p.PH, WH), td = cdiv(p.PD, WD);
+    const int64_t og = cdiv(d.O, 16 * MB);
+    const int64_t tiles = tw * th * td * d.N * og;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC>), dim3((unsigned)tiles),
+                       dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p, tiles, (int)tw, (int)th,
+                       (int)td, inv_count);
+    return hipGetLastError();
+}
+
+}  // namespace convfuse

@@ -1,0 +1,125 @@
+/*
+ * convfuse.h -- C ABI of the fused fp32 convolution library (libconvfuse.so, gfx950).
+ *
+ * Three entry points, each one fused GPU pass whose intermediate tensors never reach
+ * HBM:
+ *   conv3d_mish_tanh                 y = tanh(mish(conv3d(x) + b))
+ *   conv3d_div_maxpool_gap_bias_sum  out[n] = sum_c(mean(maxpool(conv3d(x)/divisor)) + bias[c])
+ *   dwsep_conv2d                     y = pointwise1x1(depthwise(x))
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous fp32 in PyTorch's layouts: activations NCDHW / NCHW,
+ *     Conv3d weights [Cout][Cin][k][k][k], depthwise weights [Cin][1][K][K],
+ *     pointwise weights [Cout][Cin][1][1].  All tensor pointers are DEVICE pointers
+ *     on the current HIP device.
+ *   - Convolutions are cross-correlations (no kernel flip) with zero padding.
+ *   - The caller owns every buffer, outputs included; no call allocates memory.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Inputs must stay valid and unmodified until the stream reaches the call.
+ *     Calls that share no output buffer may run concurrently on different streams.
+ *   - Return value: CONVFUSE_OK, or an error code.  Arguments are validated before
+ *     anything is launched, so a non-OK return from validation has no side effects.
+ *     convfuse_last_error() returns a message for the calling thread's last failure.
+ *   - Output sizes follow floor((in + 2*pad - dilation*(k-1) - 1)/stride) + 1
+ *     (convfuse_conv_out_len).
+ *   - Outputs are written only where they exist; ragged tiles never write past them.
+ */
+#ifndef CONVFUSE_H
+#define CONVFUSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    CONVFUSE_OK = 0,
+    CONVFUSE_ERR_NULL = 1,        /* a required pointer is NULL */
+    CONVFUSE_ERR_SHAPE = 2,       /* a size is non-positive, too large, or the output is empty */
+    CONVFUSE_ERR_UNSUPPORTED = 3, /* valid convolution parameters the GPU path does not implement */
+    CONVFUSE_ERR_DEVICE = 4       /* a HIP call or kernel launch failed */
+};
+
+/*
+ * y = tanh(mish(conv3d(x, w) + b)),  mish(v) = v * tanh(softplus(v)).
+ * Page "Kimi-K2.6 l2_p47" (Conv3d + Mish + Tanh): problem statement and the
+ * softplus-threshold paragraph (softplus(v) = v for v > 20).
+ *
+ *   x  [N][Cin][D][H][W]            device, read-only
+ *   w  [Cout][Cin][k][k][k]         device, read-only
+ *   b  [Cout] or NULL (no bias)     device, read-only
+ *   y  [N][Cout][OD][OH][OW]        device, written; OD = (D + 2*pad - k)/stride + 1, etc.
+ * Supported on the GPU: k = 3, stride = 1, 0 <= pad <= 2; any N, Cin, Cout >= 1 and any
+ * D, H, W that give a non-empty output.  Other k/stride return CONVFUSE_ERR_UNSUPPORTED.
+ * Accumulation is fp32 on fp32 matrix cores; the epilogue runs in registers.
+ */
+int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
+                     int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                     int64_t Cout, int64_t k, int64_t stride, int64_t pad, void *stream);
+
+/*
+ * out[n] = sum_c ( mean_{pd,ph,pw} maxpool_pool( (conv3d(x, w) + conv_b) / divisor )[n,c]
+ *                  + bias[c] )
+ * with a valid (stride 1, no padding) conv and a pool^3 max-pool of stride pool, floor
+ * mode.  Page "Kimi-K2.6 l2_p8" (Conv3d, /2, MaxPool3d, AdaptiveAvgPool3d, +bias, sum over
+ * channels): the opening shape walk-through and the rewrite as a sum of channel means
+ * plus the bias sum.
+ *
+ *   x       [N][Cin][D][H][W]       device, read-only
+ *   w       [Cout][Cin][k][k][k]    device, read-only
+ *   conv_b  [Cout] or NULL          device, read-only
+ *   divisor finite and non-zero (negative divisors turn the max into a min of the conv)
+ *   bias    [Cout] (the [Cout,1,1,1] tensor)  device, read-only
+ *   out     [N] (the [N,1,1,1] result)        device, written; the call initialises it,
+ *           so the caller need not clear it.
+ * The whole reduction happens on the device; nothing is synchronised with the host.  The
+ * channel/window partial sums meet through float atomics, so the last bits of out[n]
+ * may differ from run to run.
+ * Supported on the GPU: k = 3, pool = 2.  Other values return CONVFUSE_ERR_UNSUPPORTED.
+ */
+int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
+                                    float divisor, int64_t pool, const float *bias, float *out,
+                                    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                    int64_t Cout, int64_t k, void *stream);
+
+/*
+ * y = pointwise(depthwise(x)):
+ *   dw[n,c,h,w] = dw_b[c] + sum_{kh,kw} dw_w[c,0,kh,kw] * x[n,c,h*s-p+kh*d, w*s-p+kw*d]
+ *   y[n,o,h,w]  = pw_b[o] + sum_c pw_w[o,c,0,0] * dw[n,c,h,w]
+ * Page "Kimi-K2.6 l1_p86" (depthwise-separable Conv2d): the fused-definition pseudocode.
+ *
+ *   x     [N][Cin][H][W]       device, read-only
+ *   dw_w  [Cin][1][K][K]       device, read-only
+ *   dw_b  [Cin] or NULL        device, read-only
+ *   pw_w  [Cout][Cin][1][1]    device, read-only
+ *   pw_b  [Cout] or NULL       device, read-only
+ *   y     [N][Cout][Ho][Wo]    device, written; Ho = (H + 2p - d(K-1) - 1)/s + 1
+ * The depthwise result stays on chip; only y is written.
+ * Supported on the GPU: K = 3, stride = 1, dilation = 1, 0 <= pad <= 2.  Other values
+ * return CONVFUSE_ERR_UNSUPPORTED.
+ */
+int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                 const float *pw_b, float *y, int64_t N, int64_t Cin, int64_t H, int64_t W,
+                 int64_t Cout, int64_t K, int64_t stride, int64_t pad, int64_t dilation,
+                 void *stream);
+
+/* Output length of one spatial dimension, floor((in + 2*pad - dilation*(k-1) - 1)/stride)+1
+ * (page l1_p86 output-size formula).  Pure host function.  Writes *out and returns
+ * CONVFUSE_OK, or CONVFUSE_ERR_NULL / CONVFUSE_ERR_SHAPE (non-positive in, k, stride or
+ * dilation, negative pad, or an empty output). */
+int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dilation,
+                          int64_t *out);
+
+/* Message describing the calling thread's most recent failed call ("" if none).  The
+ * pointer stays valid until the thread's next failing call. */
+const char *convfuse_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int convfuse_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVFUSE_H */

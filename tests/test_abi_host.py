@@ -1,0 +1,131 @@
+"""Host-only checks of libconvfuse.so: it loads, exports every function include/convfuse.h
+declares, and rejects bad arguments with the documented codes before launching anything.
+No GPU is needed: every call here fails validation (or is an N = 0 no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import implicit_gemm_convolution_conv3d_amd as cf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "convfuse.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    assert {"conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d"} <= names
+    assert names == set(cf.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = cf.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.convfuse_abi_version() == 100
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((32, 3, 1, 0, 1), 30), ((64, 3, 1, 0, 1), 62), ((512, 3, 1, 1, 1), 512),
+    ((333, 3, 1, 1, 1), 333), ((517, 3, 1, 1, 1), 517), ((14, 2, 2, 0, 1), 7),
+    ((62, 2, 2, 0, 1), 31), ((10, 3, 2, 1, 1), 5), ((9, 3, 1, 2, 2), 9), ((1, 1, 1, 0, 1), 1),
+])
+def test_out_len(args, expected):
+    assert cf.conv_out_len(*args) == expected
+
+
+@pytest.mark.parametrize("args", [(0, 3, 1, 0, 1), (2, 3, 1, 0, 1), (5, 3, 0, 0, 1),
+                                  (5, 3, 1, -1, 1), (5, 0, 1, 0, 1), (5, 3, 1, 0, 0)])
+def test_out_len_rejects(args):
+    with pytest.raises(cf.ConvFuseError) as e:
+        cf.conv_out_len(*args)
+    assert e.value.code == cf.ERR_SHAPE
+    assert "convfuse_conv_out_len" in cf.lib().convfuse_last_error().decode()
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def call_act(x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C=4, D=8, H=8, W=8, O=8, k=3, s=1, p=0):
+    return cf.lib().conv3d_mish_tanh(x, w, b, y, N, C, D, H, W, O, k, s, p, None)
+
+
+def call_pool(x=FAKE, w=FAKE, cb=None, div=2.0, pool=2, bias=FAKE, out=FAKE, N=1, C=4, D=8,
+              H=8, W=8, O=8, k=3):
+    return cf.lib().conv3d_div_maxpool_gap_bias_sum(x, w, cb, div, pool, bias, out, N, C, D, H,
+                                                    W, O, k, None)
+
+
+def call_dw(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W=8, O=8, K=3,
+            s=1, p=1, d=1):
+    return cf.lib().dwsep_conv2d(x, dw, db, pw, pb, y, N, C, H, W, O, K, s, p, d, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(w=None), cf.ERR_NULL), (dict(y=None), cf.ERR_NULL),
+    (dict(C=0), cf.ERR_SHAPE), (dict(O=0), cf.ERR_SHAPE), (dict(N=-1), cf.ERR_SHAPE),
+    (dict(D=2), cf.ERR_SHAPE), (dict(W=0), cf.ERR_SHAPE), (dict(p=-1), cf.ERR_SHAPE),
+    (dict(s=0), cf.ERR_SHAPE), (dict(C=1 << 40), cf.ERR_SHAPE),
+    (dict(N=1 << 20, C=1 << 20, D=1 << 20, H=1 << 20), cf.ERR_SHAPE),
+    (dict(k=5), cf.ERR_UNSUPPORTED), (dict(s=2), cf.ERR_UNSUPPORTED),
+    (dict(p=3), cf.ERR_UNSUPPORTED), (dict(k=1), cf.ERR_UNSUPPORTED),
+])
+def test_conv3d_mish_tanh_validation(kw, code):
+    assert call_act(**kw) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("conv3d_mish_tanh")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(bias=None), cf.ERR_NULL), (dict(out=None), cf.ERR_NULL),
+    (dict(div=0.0), cf.ERR_SHAPE), (dict(div=float("inf")), cf.ERR_SHAPE),
+    (dict(div=float("nan")), cf.ERR_SHAPE), (dict(D=3), cf.ERR_SHAPE),
+    (dict(pool=0), cf.ERR_SHAPE), (dict(pool=9), cf.ERR_SHAPE), (dict(C=0), cf.ERR_SHAPE),
+    (dict(pool=3), cf.ERR_UNSUPPORTED), (dict(k=5), cf.ERR_UNSUPPORTED),
+])
+def test_pool_validation(kw, code):
+    assert call_pool(**kw) == code
+    assert "conv3d_div_maxpool_gap_bias_sum" in cf.lib().convfuse_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(dw=None), cf.ERR_NULL), (dict(pw=None), cf.ERR_NULL),
+    (dict(y=None), cf.ERR_NULL), (dict(C=0), cf.ERR_SHAPE), (dict(H=0), cf.ERR_SHAPE),
+    (dict(p=0, H=2), cf.ERR_SHAPE), (dict(d=0), cf.ERR_SHAPE),
+    (dict(K=5, p=2), cf.ERR_UNSUPPORTED), (dict(s=2), cf.ERR_UNSUPPORTED),
+    (dict(d=2, p=2), cf.ERR_UNSUPPORTED), (dict(p=3), cf.ERR_UNSUPPORTED),
+])
+def test_dwsep_validation(kw, code):
+    assert call_dw(**kw) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("dwsep_conv2d")
+
+
+def test_empty_batch_is_a_no_op():
+    # N = 0: nothing to compute, no pointer is needed and nothing is launched.
+    assert call_act(x=None, w=None, y=None, N=0) == cf.OK
+    assert call_pool(x=None, w=None, bias=None, out=None, N=0) == cf.OK
+    assert call_dw(x=None, dw=None, pw=None, y=None, N=0) == cf.OK
+
+
+def test_error_message_is_thread_local():
+    import threading
+    assert call_act(k=5) == cf.ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = cf.lib().convfuse_last_error().decode()
+        call_dw(C=0)
+        seen["after"] = cf.lib().convfuse_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert seen["after"].startswith("dwsep_conv2d")
+    assert cf.lib().convfuse_last_error().decode().startswith("conv3d_mish_tanh")
