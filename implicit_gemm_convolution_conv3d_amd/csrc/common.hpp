@@ -54,3 +54,80 @@ constexpr int halo_channel_stride(int plane_floats)
 }
 
 }  // namespace convfuse
+
+namespace convfuse {
+
+// Global -> register -> LDS staging of a halo box stored as ROWS rows.  Each row is MAIN
+// contiguous floats starting at global column col0 (a multiple of 4), plus two edge
+// columns (the halo: `pad` columns left of col0 and 2 - pad right of col0 + MAIN).  In
+// LDS, column 4 of a row holds global column col0, so the main part is 16-byte aligned.
+// load() issues every global load of the box before any is waited on; store() writes the
+// registers to LDS.  Columns outside [0, W) and rows the source marks as absent read as 0.
+// VEC: W % 4 == 0 and 16-byte aligned rows, so the main part moves as float4.
+template <int ROWS, int MAIN, int NT, bool VEC>
+struct HaloRows {
+    static constexpr int TPR = MAIN / 4;                 // threads per row, one float4 each
+    static constexpr int RPP = NT / TPR;                 // rows per pass
+    static constexpr int P = (ROWS + RPP - 1) / RPP;     // passes over the rows
+    static constexpr int PE = (2 * ROWS + NT - 1) / NT;  // edge values per thread
+    static_assert(MAIN % 4 == 0 && NT % TPR == 0, "row split");
+    floatx4 m[P];
+    float e[PE];
+
+    // src(row): global pointer to column 0 of the row, or nullptr for an all-zero row.
+    template <class Src>
+    __device__ __forceinline__ void load(const Src &src, int col0, int pad, int W)
+    {
+        const int t = threadIdx.x;
+        const int c = col0 + 4 * (t % TPR);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int row = t / TPR + p * RPP;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            const float *base = row < ROWS ? src(row) : nullptr;
+            if (base) {
+                if constexpr (VEC) {
+                    if (c < W) v = *reinterpret_cast<const floatx4 *>(base + c);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (c + i < W) v[i] = base[c + i];
+                }
+            }
+            m[p] = v;
+        }
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int idx = t + p * NT;
+            const int row = idx >> 1, j = idx & 1;
+            float v = 0.f;
+            if (row < ROWS) {
+                const float *base = src(row);
+                const int col = j < pad ? col0 - pad + j : col0 + MAIN + j - pad;
+                if (base && (unsigned)col < (unsigned)W) v = base[col];
+            }
+            e[p] = v;
+        }
+    }
+
+    // dst(row): LDS pointer of the row (its column 0 = global column col0 - 4).
+    template <class Dst>
+    __device__ __forceinline__ void store(const Dst &dst, int pad) const
+    {
+        const int t = threadIdx.x;
+        const int q = t % TPR;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int row = t / TPR + p * RPP;
+            if (row < ROWS) *reinterpret_cast<floatx4 *>(dst(row) + 4 + 4 * q) = m[p];
+        }
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int idx = t + p * NT;
+            const int row = idx >> 1, j = idx & 1;
+            if (row < ROWS) dst(row)[j < pad ? 4 - pad + j : 4 + MAIN + j - pad] = e[p];
+        }
+    }
+};
+
+}  // namespace convfuse

@@ -12,9 +12,10 @@
 // tap: its LDS address is a per-lane base plus a compile-time offset.
 //
 // Workgroup = WD x WH waves.  Each wave owns a box of output voxels and all 16*MB output
-// channels of its channel group; the input halo of the workgroup's box is staged into
-// LDS one chunk of CC input channels at a time, together with the chunk's weights laid
-// out in MFMA fragment order ([tap][channel group][lane][MB]).
+// channels of its channel group.  The input halo of the workgroup's box and the matching
+// weights (in A-fragment order, [tap][channel group][lane][MB]) are staged into LDS one
+// chunk of CC input channels at a time; the next chunk's global loads are issued into
+// registers before the current chunk's MFMAs, so their latency hides behind the math.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,65 +24,59 @@ namespace convfuse {
 namespace {
 
 // tanh(mish(v)), mish(v) = v * tanh(softplus(v)), softplus(v) = v for v > 20 (PyTorch's
-// threshold).  For v <= 20, tanh(log(1 + e^v)) = n / (n + 2) with n = e^v (e^v + 2): one
-// exponential and one division instead of exp, log and tanh.  For v > 20, tanh(v) rounds
-// to 1 in fp32, so mish(v) = v.
+// threshold).  For v <= 20, tanh(log(1 + e^v)) = n / (n + 2) with n = e^v (e^v + 2); for
+// v > 20, tanh(v) rounds to 1 in fp32, so mish(v) = v.  The outer tanh(m) = 1 - 2/(e^2m + 1);
+// m >= -0.31 keeps e^2m away from 0, and its overflow to +inf gives exactly 1.
 __device__ __forceinline__ float mish_tanh(float v)
 {
     float t = 1.0f;
     if (v <= 20.0f) {
-        float e = __expf(v);
-        float n = e * (e + 2.0f);
-        t = n / (n + 2.0f);
+        const float e = __expf(v);
+        const float n = e * (e + 2.0f);
+        t = __fdividef(n, n + 2.0f);
     }
-    return tanhf(v * t);
+    const float m = v * t;
+    return 1.0f - __fdividef(2.0f, __expf(2.0f * m) + 1.0f);
 }
 
-// Copy one chunk of CC input channels of the halo box [id0, id0+HD) x [ih0, ih0+HH) x
-// [iw0, iw0+HW) into LDS (channel stride CS, row stride RS).  Out-of-range voxels and
-// channels >= C read as zero (zero padding, and the zero-weight tail of the last chunk).
-template <int CC, int HD, int HH, int HW, int RS, int CS, int NT>
-__device__ __forceinline__ void stage_halo(float *__restrict__ xs, const float *__restrict__ x,
-                                           const Conv3dDims &d, int64_t n, int c0, int id0,
-                                           int ih0, int iw0)
-{
-    constexpr int total = CC * HD * HH * HW;
-    for (int e = threadIdx.x; e < total; e += NT) {
-        const int col = e % HW;
-        const int row = e / HW;
-        const int hh = row % HH;
-        const int t = row / HH;
-        const int hd = t % HD;
-        const int c = t / HD;
-        const int ci = c0 + c, id = id0 + hd, ih = ih0 + hh, iw = iw0 + col;
-        float v = 0.0f;
-        if (ci < d.C && (unsigned)id < (unsigned)d.D && (unsigned)ih < (unsigned)d.H &&
-            (unsigned)iw < (unsigned)d.W)
-            v = x[(((n * d.C + ci) * d.D + id) * d.H + ih) * d.W + iw];
-        xs[c * CS + (hd * HH + hh) * RS + col] = v;
-    }
-}
-
-// Weights of output channels [o0, o0 + 16*MB) and input channels [c0, c0 + CC), written in
-// A-fragment order: ws[((tap * CC/4 + cg) * 64 + lane) * MB + mb] holds
+// Weights of output channels [o0, o0 + 16*MB) x input channels [c0, c0 + CC), all 27 taps,
+// held in registers between the global load and the LDS store.  Thread t owns the
+// (channel, input channel) pairs t, t + NT, ...; its 27 taps are contiguous in memory.
+// LDS layout (A-fragment order): ws[((tap*CC/4 + cg)*64 + lane)*MB + mb] holds
 // w[o0 + 16*mb + lane%16][c0 + 4*cg + lane/16][tap].  Missing channels are zero.
-template <int CC, int MB, int NT>
-__device__ __forceinline__ void stage_weights(float *__restrict__ ws, const float *__restrict__ w,
-                                              const Conv3dDims &d, int o0, int c0)
-{
-    constexpr int total = MB * 16 * CC * 27;
-    for (int e = threadIdx.x; e < total; e += NT) {
-        const int tap = e % 27;
-        const int t = e / 27;
-        const int cl = t % CC;
-        const int ol = t / CC;
-        const int o = o0 + ol, c = c0 + cl;
-        float v = 0.0f;
-        if (o < d.O && c < d.C) v = w[((int64_t)o * d.C + c) * 27 + tap];
-        const int lane = (cl & 3) * 16 + (ol & 15);
-        ws[((tap * (CC / 4) + (cl >> 2)) * 64 + lane) * MB + (ol >> 4)] = v;
+template <int MB, int CC, int NT>
+struct WeightChunk {
+    static constexpr int PAIRS = 16 * MB * CC;
+    static constexpr int PP = (PAIRS + NT - 1) / NT;
+    float v[PP][27];
+
+    __device__ __forceinline__ void load(const float *__restrict__ w, const Conv3dDims &d, int o0,
+                                         int c0)
+    {
+#pragma unroll
+        for (int p = 0; p < PP; ++p) {
+            const int pair = threadIdx.x + p * NT;
+            const int o = o0 + pair / CC, c = c0 + pair % CC;
+            const bool ok = pair < PAIRS && o < d.O && c < d.C;
+            const float *src = w + ((int64_t)o * d.C + c) * 27;
+#pragma unroll
+            for (int tap = 0; tap < 27; ++tap) v[p][tap] = ok ? src[tap] : 0.0f;
+        }
     }
-}
+
+    __device__ __forceinline__ void store(float *__restrict__ ws) const
+    {
+#pragma unroll
+        for (int p = 0; p < PP; ++p) {
+            const int pair = threadIdx.x + p * NT;
+            if (pair >= PAIRS) continue;
+            const int ol = pair / CC, cl = pair % CC;
+            const int base = ((cl >> 2) * 64 + (cl & 3) * 16 + (ol & 15)) * MB + (ol >> 4);
+#pragma unroll
+            for (int tap = 0; tap < 27; ++tap) ws[tap * (CC / 4) * 64 * MB + base] = v[p][tap];
+        }
+    }
+};
 
 template <int MB>
 __device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
@@ -89,7 +84,7 @@ __device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
     if constexpr (MB % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < MB / 4; ++i) {
-            floatx4 v = *reinterpret_cast<const floatx4 *>(p + 4 * i);
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(p + 4 * i);
             a[4 * i + 0] = v[0];
             a[4 * i + 1] = v[1];
             a[4 * i + 2] = v[2];
@@ -101,9 +96,9 @@ __device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
     }
 }
 
-// The K loop shared by both epilogues.  Wave-local voxel blocks are given by NB block
-// offsets (in LDS floats, relative to the lane base); acc[mb][nb] accumulates output
-// channels 16*mb.. of block nb.
+// One chunk of the K loop: 27 taps x CC/4 channel groups.  The NB voxel blocks of the wave
+// sit at LDS offsets boff[] from the lane base; acc[mb][nb] accumulates output channels
+// 16*mb.. of block nb.
 template <int MB, int NB, int CC, int HH, int RS, int CS>
 __device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
                                             const float *__restrict__ ws, int xlane,
@@ -133,16 +128,53 @@ __device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
                 }
 }
 
+// Staging of one chunk for a workgroup whose input box is [id0, id0+HD) x [ih0, ih0+HH) x
+// columns [iw0 - pad, iw0 - pad + MAIN + 2), plus its weights.
+template <int MB, int CC, int HD, int HH, int MAIN, int RS, int CS, int NT, bool VEC>
+struct ChunkStage {
+    HaloRows<CC * HD * HH, MAIN, NT, VEC> halo;
+    WeightChunk<MB, CC, NT> wts;
+
+    __device__ __forceinline__ void load(const float *__restrict__ x, const float *__restrict__ w,
+                                         const Conv3dDims &d, int64_t n, int c0, int o0, int id0,
+                                         int ih0, int iw0)
+    {
+        auto src = [&](int row) -> const float * {
+            const int hh = row % HH, t = row / HH;
+            const int hd = t % HD, c = t / HD;
+            const int ci = c0 + c, id = id0 + hd, ih = ih0 + hh;
+            if (ci >= d.C || (unsigned)id >= (unsigned)d.D || (unsigned)ih >= (unsigned)d.H)
+                return nullptr;
+            return x + (((n * d.C + ci) * d.D + id) * d.H + ih) * d.W;
+        };
+        halo.load(src, iw0, d.pad, (int)d.W);
+        wts.load(w, d, o0, c0);
+    }
+
+    __device__ __forceinline__ void store(float *__restrict__ xs, float *__restrict__ ws,
+                                          int pad) const
+    {
+        auto dst = [&](int row) -> float * {
+            const int hh = row % HH, t = row / HH;
+            const int hd = t % HD, c = t / HD;
+            return xs + c * CS + (hd * HH + hh) * RS;
+        };
+        halo.store(dst, pad);
+        wts.store(ws);
+    }
+};
+
 // ------------------------------------------------------------------ Mish/tanh epilogue
 // Wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns [ow0, ow0 + 16*NBW).
-template <int MB, int NBW, int WD, int WH, int CC>
-__global__ __launch_bounds__(64 * WD * WH) void conv3d_mish_tanh_kernel(
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC>
+__global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
 {
     constexpr int NT = 64 * WD * WH;
-    constexpr int HD = WD + 2, HH = WH + 2, HW = 16 * NBW + 2;
-    constexpr int RS = round_up(HW, 4);
+    constexpr int MAIN = 16 * NBW;
+    constexpr int HD = WD + 2, HH = WH + 2;
+    constexpr int RS = MAIN + 8;
     constexpr int CS = halo_channel_stride(HD * HH * RS);
     constexpr int XS = CC * CS;
     constexpr int WSZ = 27 * CC * 16 * MB;
@@ -157,46 +189,56 @@ __global__ __launch_bounds__(64 * WD * WH) void conv3d_mish_tanh_kernel(
     const int64_t n = t % d.N;
     const int og = (int)(t / d.N);
 
-    const int od0 = td * WD, oh0 = th * WH, ow0 = tw * 16 * NBW, o0 = og * 16 * MB;
+    const int od0 = td * WD, oh0 = th * WH, ow0 = tw * MAIN, o0 = og * 16 * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wd = wave / WH, wh = wave % WH;
-    const int xlane = (lane >> 4) * CS + (wd * HH + wh) * RS + (lane & 15);
+    // LDS column of voxel column v at tap kw is v + kw + 4 - pad.
+    const int xlane = (lane >> 4) * CS + (wd * HH + wh) * RS + (lane & 15) + 4 - d.pad;
     int boff[NBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) boff[nb] = 16 * nb;
 
-    floatx4 acc[MB][NBW];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC> stage;
+    const int id0 = od0 - d.pad, ih0 = oh0 - d.pad;
+    stage.load(x, w, d, n, 0, o0, id0, ih0, ow0);
 
     const int od = od0 + wd, oh = oh0 + wh;
-    const bool active = od < d.OD && oh < d.OH;
-    for (int c0 = 0; c0 < d.C; c0 += CC) {
-        __syncthreads();
-        stage_halo<CC, HD, HH, HW, RS, CS, NT>(xs, x, d, n, c0, od0 - d.pad, oh0 - d.pad,
-                                               ow0 - d.pad);
-        stage_weights<CC, MB, NT>(ws, w, d, o0, c0);
-        __syncthreads();
-        if (active) igemm_chunk<MB, NBW, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
-    }
-    if (!active) return;
-
+    if (od < d.OD && oh < d.OH) {
+        floatx4 acc[MB][NBW];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
-            if (o >= d.O) continue;
-            const float bias = b ? b[o] : 0.0f;
-            float *yrow = y + (((n * d.O + o) * d.OD + od) * d.OH + oh) * d.OW;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int ow = ow0 + 16 * nb + (lane & 15);
-                if (ow < d.OW) yrow[ow] = mish_tanh(acc[mb][nb][r] + bias);
-            }
+            for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < d.C; c0 += CC) {
+            __syncthreads();
+            stage.store(xs, ws, d.pad);
+            __syncthreads();
+            if (c0 + CC < d.C) stage.load(x, w, d, n, c0 + CC, o0, id0, ih0, ow0);
+            igemm_chunk<MB, NBW, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
         }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+                if (o >= d.O) continue;
+                const float bias = b ? b[o] : 0.0f;
+                float *yrow = y + (((n * d.O + o) * d.OD + od) * d.OH + oh) * d.OW;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const int ow = ow0 + 16 * nb + (lane & 15);
+                    if (ow < d.OW) yrow[ow] = mish_tanh(acc[mb][nb][r] + bias);
+                }
+            }
+    } else {
+        // This wave's row lies past the output: it only helps stage the shared tiles.
+        for (int c0 = 0; c0 < d.C; c0 += CC) {
+            __syncthreads();
+            stage.store(xs, ws, d.pad);
+            __syncthreads();
+            if (c0 + CC < d.C) stage.load(x, w, d, n, c0 + CC, o0, id0, ih0, ow0);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ pool/sum epilogue
@@ -204,16 +246,17 @@ __global__ __launch_bounds__(64 * WD * WH) void conv3d_mish_tanh_kernel(
 // voxel blocks are (dd, dh, q): conv voxel (2pd + dd, 2ph + dh, 2pw0 + 16q + j) for lane
 // column j, so the max over (dd, dh) is taken inside a lane and the max over the window's
 // two columns between lanes j and j^1.
-template <int MB, int NBW, int WD, int WH, int CC>
-__global__ __launch_bounds__(64 * WD * WH) void conv3d_pool_sum_kernel(
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool PREFETCH>
+__global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     float *__restrict__ out, PoolDims pd_, int64_t tiles, int tiles_w, int tiles_h,
     int tiles_d, float inv_count)
 {
     constexpr int NT = 64 * WD * WH;
     constexpr int NB = 4 * NBW;
-    constexpr int HD = 2 * WD + 2, HH = 2 * WH + 2, HW = 16 * NBW + 2;
-    constexpr int RS = round_up(HW, 4);
+    constexpr int MAIN = 16 * NBW;
+    constexpr int HD = 2 * WD + 2, HH = 2 * WH + 2;
+    constexpr int RS = MAIN + 8;
     constexpr int CS = halo_channel_stride(HD * HH * RS);
     constexpr int XS = CC * CS;
     constexpr int WSZ = 27 * CC * 16 * MB;
@@ -233,58 +276,79 @@ __global__ __launch_bounds__(64 * WD * WH) void conv3d_pool_sum_kernel(
     const int pd0 = td * WD, ph0 = th * WH, pw0 = tw * 8 * NBW, o0 = og * 16 * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wd = wave / WH, wh = wave % WH;
-    const int xlane = (lane >> 4) * CS + (2 * wd * HH + 2 * wh) * RS + (lane & 15);
+    const int xlane = (lane >> 4) * CS + (2 * wd * HH + 2 * wh) * RS + (lane & 15) + 4;
     int boff[NB];
 #pragma unroll
     for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
         for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-            for (int q = 0; q < NBW; ++q) boff[(dd * 2 + dh) * NBW + q] = (dd * HH + dh) * RS + 16 * q;
+            for (int q = 0; q < NBW; ++q)
+                boff[(dd * 2 + dh) * NBW + q] = (dd * HH + dh) * RS + 16 * q;
 
-    floatx4 acc[MB][NB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC> stage;
+    auto next = [&](int c0) {
+        // With PREFETCH the chunk after c0 is loaded into registers while c0 computes;
+        // without it each chunk is loaded right before it is stored, and other resident
+        // workgroups cover the latency.
+        if constexpr (PREFETCH) {
+            if (c0 + CC < d.C) stage.load(x, w, d, n, c0 + CC, o0, 2 * pd0, 2 * ph0, 2 * pw0);
+        }
+    };
+    auto put = [&](int c0) {
+        if constexpr (!PREFETCH) stage.load(x, w, d, n, c0, o0, 2 * pd0, 2 * ph0, 2 * pw0);
+        stage.store(xs, ws, 0);
+    };
+    if constexpr (PREFETCH) stage.load(x, w, d, n, 0, o0, 2 * pd0, 2 * ph0, 2 * pw0);
 
     const int pdi = pd0 + wd, phi = ph0 + wh;
-    const bool active = pdi < pd_.PD && phi < pd_.PH;
-    for (int c0 = 0; c0 < d.C; c0 += CC) {
-        __syncthreads();
-        stage_halo<CC, HD, HH, HW, RS, CS, NT>(xs, x, d, n, c0, 2 * pd0, 2 * ph0, 2 * pw0);
-        stage_weights<CC, MB, NT>(ws, w, d, o0, c0);
-        __syncthreads();
-        if (active) igemm_chunk<MB, NB, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
-    }
-
-    // (conv + cb) / divisor is monotone in conv: increasing for a positive divisor, so the
-    // window maximum of the divided values is (max conv + cb) / divisor; for a negative
-    // divisor it is (min conv + cb) / divisor.
-    const bool use_min = pd_.divisor < 0.0f;
-    const int j = lane & 15;
     float part = 0.0f;
+    if (pdi < pd_.PD && phi < pd_.PH) {
+        floatx4 acc[MB][NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
-            const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
-#pragma unroll
-            for (int q = 0; q < NBW; ++q) {
-                float m = acc[mb][q][r];
-#pragma unroll
-                for (int p = 1; p < 4; ++p) {
-                    const float v = acc[mb][p * NBW + q][r];
-                    m = use_min ? fminf(m, v) : fmaxf(m, v);
-                }
-                const float m2 = __shfl_xor(m, 1, 64);
-                m = use_min ? fminf(m, m2) : fmaxf(m, m2);
-                const int pw = pw0 + 8 * q + (j >> 1);
-                if (active && o < d.O && (j & 1) == 0 && pw < pd_.PW)
-                    part += (m + cbv) / pd_.divisor;
-            }
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < d.C; c0 += CC) {
+            __syncthreads();
+            put(c0);
+            __syncthreads();
+            next(c0);
+            igemm_chunk<MB, NB, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
         }
+        // (conv + cb) / divisor is monotone in conv: increasing for a positive divisor, so
+        // the window maximum of the divided values is (max conv + cb) / divisor; for a
+        // negative divisor it is (min conv + cb) / divisor.
+        const bool use_min = pd_.divisor < 0.0f;
+        const int j = lane & 15;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+                const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < NBW; ++q) {
+                    float m = acc[mb][q][r];
+#pragma unroll
+                    for (int p = 1; p < 4; ++p) {
+                        const float v = acc[mb][p * NBW + q][r];
+                        m = use_min ? fminf(m, v) : fmaxf(m, v);
+                    }
+                    const float m2 = __shfl_xor(m, 1, 64);
+                    m = use_min ? fminf(m, m2) : fmaxf(m, m2);
+                    const int pw = pw0 + 8 * q + (j >> 1);
+                    if (o < d.O && (j & 1) == 0 && pw < pd_.PW) part += (m + cbv) / pd_.divisor;
+                }
+            }
+    } else {
+        for (int c0 = 0; c0 < d.C; c0 += CC) {
+            __syncthreads();
+            put(c0);
+            __syncthreads();
+            next(c0);
+        }
+    }
     part = wave_sum(part);
     if (lane == 0) red[wave] = part;
     __syncthreads();
@@ -310,6 +374,8 @@ __global__ void pool_sum_init_kernel(const float *__restrict__ bias, float *__re
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+inline bool vec_ok(const float *x, int64_t W) { return W % 4 == 0 && ((uintptr_t)x & 15) == 0; }
+
 template <int MB, int NBW, int WD, int WH, int CC>
 hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
                       const Conv3dDims &d, hipStream_t s)
@@ -318,8 +384,14 @@ hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
     const int64_t og = cdiv(d.O, 16 * MB);
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC>), dim3((unsigned)tiles),
-                       dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles, (int)tw, (int)th, (int)td);
+    if (vec_ok(x, d.W))
+        hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, true>),
+                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
+                           (int)tw, (int)th, (int)td);
+    else
+        hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, false>),
+                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
+                           (int)tw, (int)th, (int)td);
     return hipGetLastError();
 }
 
@@ -352,9 +424,14 @@ hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *c
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
-    hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC>), dim3((unsigned)tiles),
-                       dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p, tiles, (int)tw, (int)th,
-                       (int)td, inv_count);
+    if (vec_ok(x, d.W))
+        hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, true, false>),
+                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
+                           tiles, (int)tw, (int)th, (int)td, inv_count);
+    else
+        hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, false, false>),
+                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
+                           tiles, (int)tw, (int)th, (int)td, inv_count);
     return hipGetLastError();
 }
 
