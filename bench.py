@@ -82,6 +82,50 @@ def load_traffic(kernel_name):
     return ent.get("hbm_bytes_per_launch")
 
 
+KERNEL_PREFIX = {"conv3d_pool_sum_kernel": "conv3d_div_maxpool_gap_bias_sum",
+                 "conv3d_mish_tanh_kernel": "conv3d_mish_tanh",
+                 "dwsep_kernel<8": "dwsep_conv2d_512", "dwsep_kernel<12": "dwsep_conv2d_333x517_bias"}
+
+
+def summarize_traffic(fetch_csv, write_csv, calib_mib):
+    """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a device copy of calib_mib MiB
+    (the copy reads and writes exactly that many bytes)."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    calib = calib_mib * (1 << 20)
+    copy_f = max((v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower()),
+                 default=None)
+    copy_w = max((v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower()),
+                 default=None)
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy kernel found in the counter files")
+    fscale, wscale = calib / (copy_f * 1024), calib / (copy_w * 1024)
+    out = {"_about": "HBM bytes per launch = FETCH_SIZE*1024*fetch_scale + WRITE_SIZE*1024*"
+                     "write_scale; scales from a %d MiB device copy" % calib_mib,
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
+    sha = kernel_source_sha()
+    for kname, f in fetch.items():
+        for pre, wl_name in KERNEL_PREFIX.items():
+            if pre in kname and kname in write:
+                fb, wb = f * 1024 * fscale, write[kname] * 1024 * wscale
+                out[wl_name] = {"kernel": kname[:120], "kernel_source_sha": sha,
+                                "fetch_bytes": round(fb), "write_bytes": round(wb),
+                                "hbm_bytes_per_launch": round(fb + wb)}
+    dst = ROOT / "profiles" / "traffic.json"
+    dst.write_text(json.dumps(out, indent=1) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def run_op(cf, w, t, out):
     p = w.params
     if w.op == "conv3d_mish_tanh":
@@ -141,7 +185,18 @@ def main():
     ap.add_argument("--cpu-sample-frac", type=float, default=0.125,
                     help="fraction of each workload's batch the oracle baseline runs on")
     ap.add_argument("--workloads", default=",".join(map(str, BENCH_WORKLOADS)))
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times), so that "
+                         "rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE can be scaled to known bytes")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run that included --copy-calibration-mib into "
+                         "profiles/traffic.json")
+    ap.add_argument("--calibration-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.calibration_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(batch sharding needs no communication; see DESIGN.md). Run with --gpus 1.",
@@ -155,6 +210,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n}), flush=True)
+        return
     cf.lib()  # fail loudly now if the library is missing
     dev = torch.device("cuda:0")
     ids = [int(s) for s in args.workloads.split(",") if s]
