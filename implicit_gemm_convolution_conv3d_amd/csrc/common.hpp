@@ -131,3 +131,19 @@ struct HaloRows {
 };
 
 }  // namespace convfuse
+
+namespace convfuse {
+
+// Workgroup barrier for data exchanged through LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) and synchronises the workgroup, but leaves its global loads and stores in
+// flight.  __syncthreads also orders global memory and so waits for every outstanding
+// vector-memory operation, stores included.  Register operands of pending loads are still
+// waited for by the compiler where they are used.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace convfuse

@@ -6,13 +6,24 @@
 // GEMM view: output pixels x output channels, reduced over input channels.  For a 16x16x4
 // MFMA k-step, lane l forms the pixel-side operand as the depthwise output of channel
 // (4*cg + l/16) at pixel column (l%16): nine reads of the staged input halo and nine FMAs,
-// so the depthwise tile never leaves registers.  The pointwise weights of a channel chunk
-// are staged in LDS in fragment order.
+// so the depthwise tile never leaves registers.  fp32 vector work does not overlap fp32
+// matrix work on this chip, so the inner loop holds no other vector instructions.
 //
-// Workgroup = WGW waves side by side along W; each wave owns R consecutive output rows of
-// one 16-pixel column block and every output channel of its channel group, so the input is
-// read once per channel group.  The next chunk's global loads are issued into registers
-// before the current chunk's MFMAs.
+// Each wave owns R output rows x 16 pixel columns and every output channel of its channel
+// group, so the input is read once per channel group.  Workgroups are 4 waves wide (tile 64
+// columns) and WH waves tall.  Input channels stream through LDS in chunks of 16: thread t
+// stages channel (t/16)%16, column quad t%16 of its share of the halo rows (one float4 per
+// row when rows are 16-byte aligned, else four dwords); the next chunk is loaded into
+// registers while the current one computes.
+//
+// Two kernels:
+//  * persistent (all pointwise weights and depthwise taps fit in LDS next to one chunk):
+//    weights are loaded once per workgroup, in MFMA fragment order; workgroups then loop
+//    over tiles, and the first chunk of the next tile streams in while the last chunk of the
+//    current one computes.  Barriers order LDS only, and outputs leave through buffer
+//    stores with a fixed instruction count per tile, so a tile's stores drain while the
+//    next tile computes.
+//  * chunked (any size): one tile per workgroup, weights staged with every chunk.
 //
 // PIXROWS selects which MFMA operand carries the pixels.  With pixels as the A operand each
 // lane ends with 4 consecutive pixels of one output channel and stores them as one float4
@@ -25,247 +36,621 @@ namespace convfuse {
 
 namespace {
 
-// Pointwise weights of output channels [o0, o0 + 16*MB) x input channels [c0, c0 + CC),
-// stored as ps[(cg*64 + lane)*MB + mb] = pw_w[o0 + 16*mb + lane%16][c0 + 4*cg + lane/16].
-// Thread t loads the float4 quads t, t + NT, ... (quad = 4 consecutive input channels).
-template <int MB, int CC, int NT, bool VEC>
-struct PwChunk {
-    static constexpr int QUADS = 16 * MB * CC / 4;
-    static constexpr int PQ = (QUADS + NT - 1) / NT;
-    floatx4 v[PQ];
+constexpr int kDwCC = 16;  // input channels per chunk
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit access
+constexpr int kDwTW = 64;  // output tile width (4 waves x 16 columns)
 
-    __device__ __forceinline__ void load(const float *__restrict__ pw, const DwsepDims &d, int o0,
-                                         int c0)
+template <int R, int WH>
+struct DwGeom {
+    static constexpr int NWAVE = 4 * WH;
+    static constexpr int NT = 64 * NWAVE;
+    static constexpr int TH = R * WH;                  // output tile rows
+    static constexpr int HR = TH + 2;                  // halo rows
+    static_assert(HR % WH == 0, "halo rows split evenly over the row groups");
+    static constexpr int RPT = HR / WH;                // halo rows per staging thread
+    static constexpr int RS = kDwTW + 8;               // LDS row: 4 + 64 columns + edges
+    static constexpr int CS = halo_channel_stride(HR * RS);
+    static constexpr int XS = kDwCC * CS;              // one chunk of halo
+    static constexpr int EDGES = 2 * kDwCC * HR;       // edge values per chunk
+    static_assert(EDGES <= NT, "one edge value per thread");
+};
+
+// Halo rows of one chunk held in registers between global load and LDS store.
+template <int R, int WH>
+struct DwHalo {
+    floatx4 xr[DwGeom<R, WH>::RPT];
+    float edge;
+};
+
+// Load (registers) and store (LDS) of one chunk of the halo of tile (n, h0, w0).  Thread t:
+// channel sc = (t/16)%16, column quad sq = t%16, halo rows rg*RPT .. +RPT-1 (rg = t/256);
+// edge value: thread e < EDGES takes the column left of w0 or right of w0+63 of row
+// (e/(2HR), (e%(2HR))/2).  LDS row layout: column 4 + j holds global column w0 + j.
+template <int R, int WH, bool VEC>
+struct DwHaloStager {
+    using G = DwGeom<R, WH>;
+    int sc, sq, rg, ec, ehr, eoff;
+
+    __device__ __forceinline__ void init(int tid, int pad)
     {
-#pragma unroll
-        for (int p = 0; p < PQ; ++p) {
-            const int qd = threadIdx.x + p * NT;
-            const int o = o0 + qd / (CC / 4), c = c0 + 4 * (qd % (CC / 4));
-            floatx4 r = {0.f, 0.f, 0.f, 0.f};
-            if (qd < QUADS && o < d.O) {
-                const float *src = pw + (int64_t)o * d.C + c;
-                if constexpr (VEC) {
-                    if (c < d.C) r = *reinterpret_cast<const floatx4 *>(src);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (c + i < d.C) r[i] = src[i];
-                }
-            }
-            v[p] = r;
-        }
+        sc = (tid >> 4) & 15;
+        sq = tid & 15;
+        rg = tid >> 8;
+        ec = tid / (2 * G::HR);
+        const int erem = tid % (2 * G::HR);
+        ehr = erem >> 1;
+        const int ej = erem & 1;
+        eoff = ej < pad ? -pad + ej : kDwTW + ej - pad;  // edge column - w0
     }
 
-    __device__ __forceinline__ void store(float *__restrict__ ps) const
+    __device__ __forceinline__ void load(DwHalo<R, WH> &k, const float *__restrict__ x,
+                                         const DwsepDims &d, int64_t n, int h0, int w0, int c0,
+                                         int tid) const
     {
+        const int C = (int)d.C, H = (int)d.H, W = (int)d.W;
+        const int64_t plane = (int64_t)H * W;
+        const int ih0 = h0 - d.pad;
+        const int col = w0 + 4 * sq;
+        const int ci = c0 + sc;
+        const float *p = x + (n * C + ci) * plane + (int64_t)ih0 * W + col;
 #pragma unroll
-        for (int p = 0; p < PQ; ++p) {
-            const int qd = threadIdx.x + p * NT;
-            if (qd >= QUADS) continue;
-            const int ol = qd / (CC / 4), cg = qd % (CC / 4);
+        for (int i = 0; i < G::RPT; ++i) {
+            const int hr = rg * G::RPT + i;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (ci < C && (unsigned)(ih0 + hr) < (unsigned)H) {
+                const float *rp = p + (int64_t)hr * W;
+                if constexpr (VEC) {
+                    if (col < W) v = *reinterpret_cast<const floatx4 *>(rp);
+                } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ps[(cg * 64 + i * 16 + (ol & 15)) * MB + (ol >> 4)] = v[p][i];
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < W) v[e] = rp[e];
+                }
+            }
+            k.xr[i] = v;
         }
+        const int eci = c0 + ec, eih = ih0 + ehr, ecol = w0 + eoff;
+        float e = 0.0f;
+        if (tid < G::EDGES && eci < C && (unsigned)eih < (unsigned)H && (unsigned)ecol < (unsigned)W)
+            e = x[((n * C + eci) * H + eih) * (int64_t)W + ecol];
+        k.edge = e;
+    }
+
+    __device__ __forceinline__ void store(float *xs, const DwHalo<R, WH> &k, int tid) const
+    {
+        float *row = xs + sc * G::CS + rg * G::RPT * G::RS + 4 + 4 * sq;
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i) *reinterpret_cast<floatx4 *>(row + i * G::RS) = k.xr[i];
+        if (tid < G::EDGES) xs[ec * G::CS + ehr * G::RS + 4 + eoff] = k.edge;
     }
 };
 
-template <int MB, int R, int WGW, int CC, bool VEC, bool PIXROWS>
-__global__ __launch_bounds__(64 * WGW, 2) void dwsep_kernel(
-    const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
-    const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
-    DwsepDims d, int64_t tiles, int tiles_w, int tiles_h)
+// One chunk of the K loop.  xs: halo of the chunk, lane base applied; pw: fragment-order
+// pointwise weights of the chunk's first k-step, lane base applied (pw[cg*64*MB + mb] is the
+// operand of k-step cg, output block mb); dk: depthwise taps [c][12] (9 taps, bias at 9) of
+// the chunk's channel 4*cg + lane/16 at dk[cg*48].
+template <int MB, int R, int RS, int CS, bool PIXROWS>
+__device__ __forceinline__ void dw_chunk(const float *xs, const float *pw, const float *dk,
+                                         floatx4 (&acc)[MB][R])
 {
-    constexpr int NT = 64 * WGW;
-    constexpr int MAIN = 16 * WGW;
-    constexpr int HR = R + 2;
-    constexpr int RS = MAIN + 8;
-    constexpr int CS = halo_channel_stride(HR * RS);
-    constexpr int XS = CC * CS;
-    constexpr int PS = CC * 16 * MB;  // pointwise fragments of one chunk
-    constexpr int DS = CC * 12;       // depthwise weights (9) + bias, padded to 12
-    static_assert(DS <= NT, "one depthwise value per thread");
-    __shared__ __attribute__((aligned(16))) float lds[XS + PS + DS];
-    float *xs = lds;
-    float *ps = lds + XS;
-    float *ds = lds + XS + PS;
-
-    int64_t t = xcd_tile(blockIdx.x, tiles);
-    const int tw = (int)(t % tiles_w); t /= tiles_w;
-    const int th = (int)(t % tiles_h); t /= tiles_h;
-    const int64_t n = t % d.N;
-    const int og = (int)(t / d.N);
-
-    const int h0 = th * R, w0 = tw * MAIN, o0 = og * 16 * MB;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // LDS column of pixel column v at tap kw is v + kw + 4 - pad.
-    const int xlane = (lane >> 4) * CS + 16 * wave + (lane & 15) + 4 - d.pad;
-    const int ih0 = h0 - d.pad;
-
-    HaloRows<CC * HR, MAIN, NT, VEC> halo;
-    PwChunk<MB, CC, NT, VEC> pwc;
-    float dwv = 0.0f;
-    auto load = [&](int c0) {
-        auto src = [&](int row) -> const float * {
-            const int hr = row % HR, c = row / HR;
-            const int ci = c0 + c, ih = ih0 + hr;
-            if (ci >= d.C || (unsigned)ih >= (unsigned)d.H) return nullptr;
-            return x + ((n * d.C + ci) * d.H + ih) * d.W;
-        };
-        halo.load(src, w0, d.pad, (int)d.W);
-        pwc.load(pw_w, d, o0, c0);
-        const int k = threadIdx.x % 12, ci = c0 + threadIdx.x / 12;
-        dwv = 0.0f;
-        if (threadIdx.x < DS && ci < d.C) {
-            if (k < 9) dwv = dw_w[(int64_t)ci * 9 + k];
-            else if (k == 9 && dw_b) dwv = dw_b[ci];
+#pragma unroll
+    for (int cg = 0; cg < kDwCC / 4; ++cg) {
+        const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg);
+        const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 4);
+        const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 8);
+        const float kw9[9] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3], k2[0]};
+        const float dbias = k2[1];
+        float pwf[MB];
+#pragma unroll
+        for (int i = 0; i < MB / 4; ++i) {
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(pw + cg * 64 * MB + 4 * i);
+            pwf[4 * i + 0] = v[0];
+            pwf[4 * i + 1] = v[1];
+            pwf[4 * i + 2] = v[2];
+            pwf[4 * i + 3] = v[3];
         }
-    };
-    auto store = [&]() {
-        auto dst = [&](int row) -> float * {
-            const int hr = row % HR, c = row / HR;
-            return xs + c * CS + hr * RS;
-        };
-        halo.store(dst, d.pad);
-        pwc.store(ps);
-        if (threadIdx.x < DS) ds[threadIdx.x] = dwv;
-    };
-
-    load(0);
-    if (w0 + 16 * wave < d.Wo) {
-        floatx4 acc[MB][R];
+        float xv[R + 2][3];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int hr = 0; hr < R + 2; ++hr)
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[mb][r] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < d.C; c0 += CC) {
-            __syncthreads();
-            store();
-            __syncthreads();
-            if (c0 + CC < d.C) load(c0 + CC);
+            for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = xs[4 * cg * CS + hr * RS + kw];
 #pragma unroll
-            for (int cg = 0; cg < CC / 4; ++cg) {
-                const float *dwp = ds + (4 * cg + (lane >> 4)) * 12;
-                const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dwp);
-                const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dwp + 4);
-                const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dwp + 8);
-                const float kw9[9] = {k0[0], k0[1], k0[2], k0[3], k1[0],
-                                      k1[1], k1[2], k1[3], k2[0]};
-                const float dbias = k2[1];
-                float pwf[MB];
+        for (int r = 0; r < R; ++r) {
+            float v = dbias;
 #pragma unroll
-                for (int i = 0; i < MB / 4; ++i) {
-                    const floatx4 v =
-                        *reinterpret_cast<const floatx4 *>(ps + (cg * 64 + lane) * MB + 4 * i);
-                    pwf[4 * i + 0] = v[0];
-                    pwf[4 * i + 1] = v[1];
-                    pwf[4 * i + 2] = v[2];
-                    pwf[4 * i + 3] = v[3];
-                }
-                float xv[HR][3];
+            for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
-                for (int hr = 0; hr < HR; ++hr)
-#pragma unroll
-                    for (int kw = 0; kw < 3; ++kw)
-                        xv[hr][kw] = xs[xlane + 4 * cg * CS + hr * RS + kw];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float v = dbias;
-#pragma unroll
-                    for (int kh = 0; kh < 3; ++kh)
-#pragma unroll
-                        for (int kw = 0; kw < 3; ++kw)
-                            v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        if constexpr (PIXROWS)
-                            acc[mb][r] = mfma_16x16x4(v, pwf[mb], acc[mb][r]);
-                        else
-                            acc[mb][r] = mfma_16x16x4(pwf[mb], v, acc[mb][r]);
-                    }
-                }
-            }
-        }
-
-        if constexpr (PIXROWS) {
-            // lane holds pixels w0 + 16*wave + 4*(lane/16) + 0..3 of channel 16*mb + lane%16
-            const int wcol = w0 + 16 * wave + 4 * (lane >> 4);
+                for (int kw = 0; kw < 3; ++kw) v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const int o = o0 + 16 * mb + (lane & 15);
-                if (o >= d.O) continue;
-                const float bias = pw_b ? pw_b[o] : 0.0f;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (h0 + r >= d.Ho) continue;
-                    float *yp = y + ((n * d.O + o) * d.Ho + h0 + r) * d.Wo + wcol;
-                    const floatx4 v = acc[mb][r] + bias;
-                    if (wcol + 3 < d.Wo) {
-                        *reinterpret_cast<floatx4 *>(yp) = v;
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (wcol + i < d.Wo) yp[i] = v[i];
-                    }
-                }
+                if constexpr (PIXROWS)
+                    acc[mb][r] = mfma_16x16x4(v, pwf[mb], acc[mb][r]);
+                else
+                    acc[mb][r] = mfma_16x16x4(pwf[mb], v, acc[mb][r]);
             }
-        } else {
-            // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel w0 + 16*wave + lane%16
-            const int wcol = w0 + 16 * wave + (lane & 15);
-            if (wcol < d.Wo) {
+        }
+    }
+}
+
+// Store one wave's R x 16 outputs of output channels [obase, obase + ocnt).
+template <int MB, int R, bool PIXROWS>
+__device__ __forceinline__ void dw_epilogue(float *__restrict__ y, const DwsepDims &d, int64_t n,
+                                            int hbase, int wcol0, int obase, int ocnt,
+                                            const floatx4 (&acc)[MB][R])
+{
+    const int lane = threadIdx.x & 63;
+    if constexpr (PIXROWS) {
+        // lane holds pixels wcol0 + 4*(lane/16) + 0..3 of channel 16*mb + lane%16
+        const int wcol = wcol0 + 4 * (lane >> 4);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            const int ol = 16 * mb + (lane & 15);
+            if (ol >= ocnt) continue;
+            float *yp = y + ((n * d.O + obase + ol) * d.Ho + hbase) * d.Wo + wcol;
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int o = o0 + 16 * mb + 4 * (lane >> 4) + r4;
-                        if (o >= d.O) continue;
-                        const float bias = pw_b ? pw_b[o] : 0.0f;
-                        float *yp = y + ((n * d.O + o) * d.Ho + h0) * d.Wo + wcol;
+            for (int r = 0; r < R; ++r) {
+                if (hbase + r >= d.Ho) continue;
+                if (wcol + 3 < d.Wo) {
+                    *reinterpret_cast<floatx4 *>(yp + (int64_t)r * d.Wo) = acc[mb][r];
+                } else {
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            if (h0 + r < d.Ho) yp[(int64_t)r * d.Wo] = acc[mb][r][r4] + bias;
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        if (wcol + i < d.Wo) yp[(int64_t)r * d.Wo + i] = acc[mb][r][i];
+                }
             }
         }
     } else {
+        // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16
+        const int wcol = wcol0 + (lane & 15);
+        if (wcol >= d.Wo) return;
+        int64_t cstride = (int64_t)d.Ho * d.Wo;
+        // Opaque to the optimiser: keeps the per-channel offsets from being hoisted out of
+        // the caller's tile loop, where they would pin dozens of scalar registers.
+        asm volatile("" : "+s"(cstride));
+        float *yp = y + ((n * d.O + obase + 4 * (lane >> 4)) * d.Ho + hbase) * d.Wo + wcol;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ol = 16 * mb + 4 * (lane >> 4) + r4;
+                if (ol < ocnt) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (hbase + r < d.Ho) yp[(int64_t)r * d.Wo] = acc[mb][r][r4];
+                }
+                yp += r4 == 3 ? 13 * cstride : cstride;
+            }
+    }
+}
+
+// Accumulators start at the pointwise bias.  bs[16*mb + j] is the bias of output channel
+// obase + 16*mb + j (0 past the slice or without bias).
+template <int MB, int R, bool PIXROWS>
+__device__ __forceinline__ void acc_init(floatx4 (&acc)[MB][R], const float *bs)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        floatx4 b;
+        if constexpr (PIXROWS) {
+            const float v = bs[16 * mb + (lane & 15)];
+            b = floatx4{v, v, v, v};
+        } else {
+            b = *reinterpret_cast<const floatx4 *>(bs + 16 * mb + 4 * (lane >> 4));
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[mb][r] = b;
+    }
+}
+
+// ----------------------------------------------------------------- persistent kernel
+// Output stores through a buffer resource: a lane whose output lies outside the tensor gets
+// an offset past the resource's range, which the hardware drops.  Every tile thus issues the
+// same number of store instructions on every path, and the compiler can wait for the next
+// tile's prefetched loads (issued before these stores) without waiting for the stores.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDropOffset = 0x80000000;  // >= kBufRange: the access is dropped
+constexpr int kBufRange = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(float *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kBufRange, kBufferWord3);
+}
+
+// Store one wave's R x 16 outputs of output channels [obase, obase + ocnt): tb points at
+// (n, obase, row h0, column 0); the wave's rows start at h0 + hrow0, its columns at wcol0.
+// Byte offsets from tb stay below 2^31 (checked by the host).
+template <int MB, int R, bool PIXROWS>
+__device__ __forceinline__ void dw_epilogue_buf(float *tb, const DwsepDims &d, int hrow0,
+                                                int hleft, int wcol0, int ocnt,
+                                                const floatx4 (&acc)[MB][R])
+{
+    const int lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rs = store_rsrc(tb);
+    int plane = (int)(d.Ho * d.Wo);  // < 2^25 here
+    int wo = (int)d.Wo;
+    // Opaque to the optimiser: keeps the per-store offsets and lane masks from being hoisted
+    // out of the caller's tile loop, where they would pin dozens of scalar registers.
+    asm volatile("" : "+s"(plane), "+s"(wo), "+s"(ocnt));
+    if constexpr (PIXROWS) {
+        // lane holds pixels wcol0 + 4*(lane/16) + 0..3 of channel 16*mb + lane%16
+        // (output rows are 16-byte aligned and Wo % 4 == 0: a quad is wholly in or out)
+        const int wcol = wcol0 + 4 * (lane >> 4);
+        const int vbase = 4 * ((lane & 15) * plane + hrow0 * wo + wcol);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const bool ok = 16 * mb + (lane & 15) < ocnt && r < hleft && wcol < wo;
+                const int off = ok ? vbase + 4 * (16 * mb * plane + r * wo) : kDropOffset;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mb][r]), rs,
+                                                       off, 0, 0);
+            }
+    } else {
+        // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16
+        const int wcol = wcol0 + (lane & 15);
+        int vmb = 4 * (4 * (lane >> 4) * plane + hrow0 * wo + wcol);  // channel block mb
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const bool ok = 16 * mb + 4 * (lane >> 4) + r4 < ocnt && r < hleft && wcol < wo;
+                    const int off = ok ? vmb + 4 * (r4 * plane + r * wo) : kDropOffset;
+                    // (a vector element is copied out first: bit-casting the element
+                    // expression itself would reinterpret the vector's first element)
+                    const float v = acc[mb][r][r4];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
+                }
+            vmb += 64 * plane;
+            asm volatile("" : "+v"(vmb));  // one running offset, not MB*4*R folded constants
+        }
+    }
+}
+
+// Fill `total` LDS slots: element e (value(e), typically a global load) goes to
+// dst[slot(e)].  B global loads per thread are in flight before the first LDS write.
+template <int NT, int B, class V, class S>
+__device__ __forceinline__ void lds_fill(float *dst, int total, const V &value, const S &slot)
+{
+    for (int base = threadIdx.x; base < total; base += B * NT) {
+        float v[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int e = base + u * NT;
+            v[u] = e < total ? value(e) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int e = base + u * NT;
+            if (e < total) dst[slot(e)] = v[u];
+        }
+    }
+}
+
+// Dynamic LDS: [halo chunk XS][pointwise fragments KS*64*MB][depthwise taps 4*KS*12]
+// [pointwise bias 16*MB], KS = 4*ceil(C/16) k-steps (whole chunks; zero past C).  Fragment
+// order: pwall[(s*64 + lane)*MB + mb] = pw_w[obase + 16*mb + lane%16][4*s + lane/16].
+template <int MB>
+constexpr size_t dw_weight_floats(int64_t C)
+{
+    const int64_t KS = (C + kDwCC - 1) / kDwCC * (kDwCC / 4);
+    return (size_t)(KS * 64 * MB + 4 * KS * 12 + 16 * MB);
+}
+
+template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+__global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
+    const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
+    const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
+    DwsepDims d, int obase, int64_t tiles, int tiles_w, int tiles_h)
+{
+    using G = DwGeom<R, WH>;
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    const int C = (int)d.C;  // small: the weights fit in LDS
+    const int KS = (C + kDwCC - 1) / kDwCC * (kDwCC / 4);
+    float *xs = dyn;
+    float *pwall = dyn + G::XS;
+    float *dkall = pwall + KS * 64 * MB;
+    float *bs = dkall + 4 * KS * 12;
+    const int ocnt = (int)(d.O - obase < 16 * MB ? d.O - obase : 16 * MB);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ww = wave & 3, wh = wave >> 2;
+
+    // Weights, once per workgroup.  Pointwise rows are read along input channels and placed
+    // at their fragment slots.
+    const int K4 = 4 * KS;
+    lds_fill<G::NT, 8>(
+        pwall, 16 * MB * K4,
+        [&](int e) {
+            const int ol = e / K4, c = e - ol * K4;
+            return (ol < ocnt && c < C) ? pw_w[(int64_t)(obase + ol) * C + c] : 0.0f;
+        },
+        [&](int e) {
+            const int ol = e / K4, c = e - ol * K4;
+            return ((c >> 2) * 64 + (c & 3) * 16 + (ol & 15)) * MB + (ol >> 4);
+        });
+    lds_fill<G::NT, 4>(
+        dkall, K4 * 12,
+        [&](int e) {
+            const int c = e / 12, k = e - c * 12;
+            float v = 0.0f;
+            if (c < C) {
+                if (k < 9) v = dw_w[(int64_t)c * 9 + k];
+                else if (k == 9 && dw_b) v = dw_b[c];
+            }
+            return v;
+        },
+        [](int e) { return e; });
+    if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
+
+    DwHaloStager<R, WH, VEC> hs;
+    hs.init(tid, d.pad);
+    // lane bases: halo (pixel column 16*ww + j, rows R*wh ..; tap kw reads LDS column
+    // 16*ww + j + kw + 4 - pad), pointwise fragments, depthwise taps of channel lane/16
+    const float *xl = xs + (lane >> 4) * G::CS + R * wh * G::RS + 16 * ww + (lane & 15) + 4 - d.pad;
+    const float *pl = pwall + lane * MB;
+    const float *dl = dkall + (lane >> 4) * 12;
+
+    auto decode = [&](int64_t tile, int64_t &n, int &h0, int &w0) {
+        int64_t t = xcd_tile(tile, tiles);
+        const int tw = (int)(t % tiles_w);
+        t /= tiles_w;
+        const int th = (int)(t % tiles_h);
+        n = t / tiles_h;
+        h0 = th * G::TH;
+        w0 = tw * kDwTW;
+    };
+
+    // Per chunk: load the next chunk (after the last one, chunk 0 of the next tile) into
+    // registers, compute this one, stage the next one.  After a tile's last chunk the outputs
+    // are stored before the staging; that staging is reached on this one path, so its wait
+    // covers the prefetched loads and not the stores issued after them.
+    int64_t tile = blockIdx.x, n;
+    int h0, w0;
+    decode(tile, n, h0, w0);
+    DwHalo<R, WH> k;
+    hs.load(k, x, d, n, h0, w0, 0, tid);
+    lds_barrier();  // weights written; no wave reads the halo buffer yet
+    hs.store(xs, k, tid);
+    lds_barrier();
+    floatx4 acc[MB][R];
+    for (;;) {
+        acc_init<MB, R, PIXROWS>(acc, bs);
+        const int64_t ntile = tile + gridDim.x;
+        int64_t nn = 0;
+        int nh0 = 0, nw0 = 0;
+        for (int c0 = 0;; c0 += kDwCC) {
+            const bool last = c0 + kDwCC >= C;
+            int64_t ln = n;
+            int lh = h0, lw = w0, lc = c0 + kDwCC;
+            if (last) {
+                if (ntile < tiles) decode(ntile, nn, nh0, nw0);
+                ln = nn;
+                lh = nh0;
+                lw = nw0;
+                lc = 0;
+            }
+            if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc, tid);
+            dw_chunk<MB, R, G::RS, G::CS, PIXROWS>(xl, pl + (c0 / 4) * 64 * MB, dl + c0 * 12, acc);
+            if (last) break;
+            lds_barrier();
+            hs.store(xs, k, tid);
+            lds_barrier();
+        }
+        float *tb = y + ((n * d.O + obase) * d.Ho + h0) * d.Wo;
+        dw_epilogue_buf<MB, R, PIXROWS>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
+                                        ocnt, acc);
+        if (ntile >= tiles) break;
+        tile = ntile;
+        n = nn;
+        h0 = nh0;
+        w0 = nw0;
+        lds_barrier();
+        hs.store(xs, k, tid);
+        lds_barrier();
+    }
+}
+
+// ----------------------------------------------------------------- chunked kernel
+// One tile per workgroup (4 waves, R rows x 64 columns); pointwise weights (fragment order)
+// and depthwise taps of each chunk are staged with the chunk.
+template <int MB>
+struct DwWeightChunk {
+    static constexpr int QUADS = 16 * MB * kDwCC / 4;
+    static constexpr int PQ = (QUADS + 255) / 256;
+    floatx4 pw[PQ];
+    float dw;
+};
+
+template <int MB, int R, bool VEC, bool PIXROWS>
+__global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
+    const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
+    const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
+    DwsepDims d, int obase, int64_t tiles, int tiles_w, int tiles_h)
+{
+    using G = DwGeom<R, 1>;
+    using WC = DwWeightChunk<MB>;
+    constexpr int PS = kDwCC * 16 * MB, DS = kDwCC * 12;
+    __shared__ __attribute__((aligned(16))) float lds[G::XS + PS + DS + 16 * MB];
+    float *xs = lds;
+    float *ps = lds + G::XS;
+    float *ds = lds + G::XS + PS;
+    float *bs = ds + DS;
+    const int C = (int)d.C;
+    const int ocnt = (int)(d.O - obase < 16 * MB ? d.O - obase : 16 * MB);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w);
+    t /= tiles_w;
+    const int th = (int)(t % tiles_h);
+    const int64_t n = t / tiles_h;
+    const int h0 = th * R, w0 = tw * kDwTW;
+
+    DwHaloStager<R, 1, VEC> hs;
+    hs.init(tid, d.pad);
+    auto wload = [&](WC &wc, int c0) {
+#pragma unroll
+        for (int p = 0; p < WC::PQ; ++p) {
+            const int qd = tid + 256 * p;
+            const int ol = qd >> 2, c = c0 + 4 * (qd & 3);
+            floatx4 r = {0.f, 0.f, 0.f, 0.f};
+            if (qd < WC::QUADS && ol < ocnt) {
+                const float *src = pw_w + (int64_t)(obase + ol) * C + c;
+                if constexpr (VEC) {
+                    if (c < C) r = *reinterpret_cast<const floatx4 *>(src);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (c + i < C) r[i] = src[i];
+                }
+            }
+            wc.pw[p] = r;
+        }
+        const int dc = c0 + tid / 12, dk = tid % 12;
+        float v = 0.0f;
+        if (tid < DS && dc < C) {
+            if (dk < 9) v = dw_w[(int64_t)dc * 9 + dk];
+            else if (dk == 9 && dw_b) v = dw_b[dc];
+        }
+        wc.dw = v;
+    };
+    auto wstore = [&](const WC &wc) {
+#pragma unroll
+        for (int p = 0; p < WC::PQ; ++p) {
+            const int qd = tid + 256 * p;
+            if (qd >= WC::QUADS) continue;
+            const int ol = qd >> 2, cg = qd & 3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ps[(cg * 64 + i * 16 + (ol & 15)) * MB + (ol >> 4)] = wc.pw[p][i];
+        }
+        if (tid < DS) ds[tid] = wc.dw;
+    };
+
+    const float *xl = xs + (lane >> 4) * G::CS + 16 * wave + (lane & 15) + 4 - d.pad;
+    const float *pl = ps + lane * MB;
+    const float *dl = ds + (lane >> 4) * 12;
+    const bool active = w0 + 16 * wave < d.Wo;
+
+    DwHalo<R, 1> k;
+    WC wc;
+    hs.load(k, x, d, n, h0, w0, 0, tid);
+    wload(wc, 0);
+    if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
+    if (active) {
+        floatx4 acc[MB][R];
+        for (int c0 = 0; c0 < C; c0 += kDwCC) {
+            lds_barrier();
+            hs.store(xs, k, tid);
+            wstore(wc);
+            lds_barrier();
+            if (c0 == 0) acc_init<MB, R, PIXROWS>(acc, bs);
+            if (c0 + kDwCC < C) {
+                hs.load(k, x, d, n, h0, w0, c0 + kDwCC, tid);
+                wload(wc, c0 + kDwCC);
+            }
+            dw_chunk<MB, R, G::RS, G::CS, PIXROWS>(xl, pl, dl, acc);
+        }
+        dw_epilogue<MB, R, PIXROWS>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
+    } else {
         // This wave's columns lie past the output: it only helps stage the shared tiles.
-        for (int c0 = 0; c0 < d.C; c0 += CC) {
-            __syncthreads();
-            store();
-            __syncthreads();
-            if (c0 + CC < d.C) load(c0 + CC);
+        for (int c0 = 0; c0 < C; c0 += kDwCC) {
+            lds_barrier();
+            hs.store(xs, k, tid);
+            wstore(wc);
+            lds_barrier();
+            if (c0 + kDwCC < C) {
+                hs.load(k, x, d, n, h0, w0, c0 + kDwCC, tid);
+                wload(wc, c0 + kDwCC);
+            }
         }
     }
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <int MB, int R, int WGW, int CC, bool VEC, bool PIXROWS>
-hipError_t launch_t(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
-                    const float *pw_b, float *y, const DwsepDims &d, hipStream_t s)
+int cu_count()
 {
-    const int64_t tw = cdiv(d.Wo, 16 * WGW), th = cdiv(d.Ho, R), og = cdiv(d.O, 16 * MB);
-    const int64_t tiles = tw * th * d.N * og;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    return cus;
+}
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_b,
+                             const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
+                             int obase, size_t lds, int per_cu, hipStream_t s)
+{
+    using G = DwGeom<R, WH>;
+    auto kern = dwsep_persistent_kernel<MB, R, WH, VEC, PIXROWS>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, G::TH);
+    const int64_t tiles = tw * th * d.N;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dwsep_kernel<MB, R, WGW, CC, VEC, PIXROWS>), dim3((unsigned)tiles),
-                       dim3(64 * WGW), 0, s, x, dw_w, dw_b, pw_w, pw_b, y, d, tiles, (int)tw,
+    // resident workgroups, a multiple of the XCD count so each stays on one XCD's tiles
+    int64_t grid = (int64_t)per_cu * cu_count() / kNumXcd * kNumXcd;
+    if (grid < 1) grid = 1;
+    if (grid > tiles) grid = tiles;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), lds, s, x, dw_w, dw_b, pw_w, pw_b,
+                       y, d, obase, tiles, (int)tw, (int)th);
+    return hipGetLastError();
+}
+
+template <int MB, int R, bool VEC, bool PIXROWS>
+hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                          const float *pw_b, float *y, const DwsepDims &d, int obase,
+                          hipStream_t s)
+{
+    const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, R);
+    const int64_t tiles = tw * th * d.N;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, PIXROWS>), dim3((unsigned)tiles),
+                       dim3(256), 0, s, x, dw_w, dw_b, pw_w, pw_b, y, d, obase, tiles, (int)tw,
                        (int)th);
     return hipGetLastError();
 }
 
-template <int MB, int R, int WGW, int CC>
-hipError_t launch(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
-                  const float *pw_b, float *y, const DwsepDims &d, hipStream_t s)
+// Pick the kernel for output channels [obase, obase + min(16*MB, O - obase)).
+template <int MB, int R, bool VEC, bool PIXROWS>
+hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                        const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
-    // Loads move as float4 when input rows and pointwise rows are 16-byte aligned; stores
-    // do when output rows are.
+    const size_t wbytes = 4 * dw_weight_floats<MB>(d.C);
+    // two 4-wave workgroups per CU, else one 8-wave workgroup, else the chunked kernel
+    const size_t lds1 = wbytes + 4 * (size_t)DwGeom<R, 1>::XS;
+    const size_t lds2 = wbytes + 4 * (size_t)DwGeom<R, 2>::XS;
+    // the persistent kernel addresses one tile's outputs with 32-bit byte offsets
+    const bool small_planes = 64 * MB * d.Ho * d.Wo <= kBufRange;
+    if (small_planes && 2 * lds1 <= kLdsBytes)
+        return launch_persistent<MB, R, 1, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase,
+                                                         lds1, 2, s);
+    if (small_planes && lds2 <= kLdsBytes)
+        return launch_persistent<MB, R, 2, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase,
+                                                         lds2, 1, s);
+    return launch_chunked<MB, 2, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+}
+
+template <int MB, int R>
+hipError_t launch(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                  const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
+{
+    // float4 loads need 16-byte aligned input and pointwise rows; float4 stores need
+    // 16-byte aligned output rows.
     const bool vin = d.W % 4 == 0 && d.C % 4 == 0 && ((uintptr_t)x & 15) == 0 &&
                      ((uintptr_t)pw_w & 15) == 0;
     const bool vout = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
-    if (vin && vout) return launch_t<MB, R, WGW, CC, true, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
-    if (vin) return launch_t<MB, R, WGW, CC, true, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
-    if (vout) return launch_t<MB, R, WGW, CC, false, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
-    return launch_t<MB, R, WGW, CC, false, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
+    if (vin && vout) return launch_slice<MB, R, true, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vin) return launch_slice<MB, R, true, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vout) return launch_slice<MB, R, false, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    return launch_slice<MB, R, false, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
 }
 
 }  // namespace
@@ -274,9 +659,15 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
                                const float *pw_w, const float *pw_b, float *y,
                                const DwsepDims &d, hipStream_t s)
 {
-    if (d.O <= 64) return launch<4, 4, 4, 16>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
-    if (d.O <= 128) return launch<8, 4, 4, 16>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
-    return launch<12, 2, 4, 16>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
+    // One launch covers up to 192 output channels; wider layers run as several launches over
+    // consecutive output-channel slices (each rereads the input).
+    if (d.O <= 64) return launch<4, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
+    if (d.O <= 128) return launch<8, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
+    for (int64_t o0 = 0; o0 < d.O; o0 += 192) {
+        const hipError_t e = launch<12, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, (int)o0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace convfuse
