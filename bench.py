@@ -82,15 +82,17 @@ def load_traffic(kernel_name):
     return ent.get("hbm_bytes_per_launch")
 
 
+# kernel name prefix (as rocprofv3 prints it) -> workload it serves in the bench step
 KERNEL_PREFIX = {"conv3d_pool_sum_kernel": "conv3d_div_maxpool_gap_bias_sum",
                  "conv3d_mish_tanh_kernel": "conv3d_mish_tanh",
-                 "dwsep_kernel<8": "dwsep_conv2d_512", "dwsep_kernel<12": "dwsep_conv2d_333x517_bias"}
+                 "dwsep_persistent_kernel<8,": "dwsep_conv2d_512",
+                 "dwsep_persistent_kernel<12,": "dwsep_conv2d_333x517_bias"}
 
 
 def summarize_traffic(fetch_csv, write_csv, calib_mib):
     """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by what the same counter reads for a device copy of calib_mib MiB
-    (the copy reads and writes exactly that many bytes)."""
+    dispatch), each scaled by what the same counter reads for a device multiply over calib_mib MiB
+    (the multiply reads and writes exactly that many bytes)."""
     import csv
 
     def per_kernel(path, counter):
@@ -103,15 +105,14 @@ def summarize_traffic(fetch_csv, write_csv, calib_mib):
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     calib = calib_mib * (1 << 20)
-    copy_f = max((v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower()),
-                 default=None)
-    copy_w = max((v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower()),
-                 default=None)
+    # the calibration kernel is torch's elementwise multiply (reads and writes calib bytes)
+    copy_f = max((v for k, v in fetch.items() if "MulFunctor" in k), default=None)
+    copy_w = max((v for k, v in write.items() if "MulFunctor" in k), default=None)
     if not copy_f or not copy_w:
-        raise SystemExit("no copy kernel found in the counter files")
+        raise SystemExit("no calibration multiply kernel found in the counter files")
     fscale, wscale = calib / (copy_f * 1024), calib / (copy_w * 1024)
     out = {"_about": "HBM bytes per launch = FETCH_SIZE*1024*fetch_scale + WRITE_SIZE*1024*"
-                     "write_scale; scales from a %d MiB device copy" % calib_mib,
+                     "write_scale; scales from a %d MiB device multiply (read + write)" % calib_mib,
            "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
     sha = kernel_source_sha()
     for kname, f in fetch.items():
@@ -182,15 +183,16 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-frac", type=float, default=0.125,
+    ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of each workload's batch the oracle baseline runs on")
     ap.add_argument("--workloads", default=",".join(map(str, BENCH_WORKLOADS)))
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (3 times), so that "
-                         "rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE can be scaled to known bytes")
+                    help="before the benchmark, run a device multiply over this many MiB "
+                         "(3 times), so that rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE of the same "
+                         "run can be scaled to known bytes")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
-                         "WRITE_SIZE) of a run that included --copy-calibration-mib into "
+                         "WRITE_SIZE) of runs that included --copy-calibration-mib into "
                          "profiles/traffic.json")
     ap.add_argument("--calibration-mib", type=int, default=1024)
     args = ap.parse_args()
@@ -215,10 +217,11 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 2.0, out=dst)  # one elementwise kernel: reads n floats, writes n
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 4 * n}), flush=True)
-        return
+        del src, dst
+        torch.cuda.empty_cache()
     cf.lib()  # fail loudly now if the library is missing
     dev = torch.device("cuda:0")
     ids = [int(s) for s in args.workloads.split(",") if s]
@@ -275,7 +278,7 @@ def main():
     dmacs, dbytes = work(dominant)
     kname = {"conv3d_mish_tanh": "conv3d_mish_tanh_kernel",
              "conv3d_div_maxpool_gap_bias_sum": "conv3d_pool_sum_kernel",
-             "dwsep_conv2d": "dwsep_kernel"}[dominant.op]
+             "dwsep_conv2d": "dwsep_persistent_kernel"}[dominant.op]
     achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),

@@ -40,6 +40,19 @@ constexpr int kDwCC = 16;  // input channels per chunk
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit access
 constexpr int kDwTW = 64;  // output tile width (4 waves x 16 columns)
 
+// Buffer-resource access.  An offset at or past the resource's range is dropped by the
+// hardware (loads return 0, stores write nothing), so padding and ragged edges need no
+// branches, and a tile issues the same memory instructions on every path.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDropOffset = 0x80000000;  // >= kBufRange: the access is dropped
+constexpr int kBufRange = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, kBufRange,
+                                             kBufferWord3);
+}
+
 template <int R, int WH>
 struct DwGeom {
     static constexpr int NWAVE = 4 * WH;
@@ -66,7 +79,9 @@ struct DwHalo {
 // channel sc = (t/16)%16, column quad sq = t%16, halo rows rg*RPT .. +RPT-1 (rg = t/256);
 // edge value: thread e < EDGES takes the column left of w0 or right of w0+63 of row
 // (e/(2HR), (e%(2HR))/2).  LDS row layout: column 4 + j holds global column w0 + j.
-template <int R, int WH, bool VEC>
+// BUF: loads through a buffer resource over image n (its byte size below 2^31), with
+// dropped offsets for the zero padding, instead of branches around plain loads.
+template <int R, int WH, bool VEC, bool BUF>
 struct DwHaloStager {
     using G = DwGeom<R, WH>;
     int sc, sq, rg, ec, ehr, eoff;
@@ -92,6 +107,35 @@ struct DwHaloStager {
         const int ih0 = h0 - d.pad;
         const int col = w0 + 4 * sq;
         const int ci = c0 + sc;
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(x + n * C * plane);
+            const bool cok = ci < C;
+            // (channel clamped so that the unused offsets of absent channels stay in range)
+            const int base = 4 * (((cok ? ci : 0) * H + ih0) * W + col);
+#pragma unroll
+            for (int i = 0; i < G::RPT; ++i) {
+                const int hr = rg * G::RPT + i;
+                const bool rok = cok && (unsigned)(ih0 + hr) < (unsigned)H;
+                if constexpr (VEC) {
+                    const int off = rok && col < W ? base + 4 * hr * W : kDropOffset;
+                    k.xr[i] = __builtin_bit_cast(
+                        floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int off = rok && col + e < W ? base + 4 * (hr * W + e) : kDropOffset;
+                        k.xr[i][e] =
+                            __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                    }
+                }
+            }
+            const int eci = c0 + ec, eih = ih0 + ehr, ecol = w0 + eoff;
+            const bool eok = tid < G::EDGES && eci < C && (unsigned)eih < (unsigned)H &&
+                             (unsigned)ecol < (unsigned)W;
+            const int eoffb = eok ? 4 * (((eci < C ? eci : 0) * H + eih) * W + ecol) : kDropOffset;
+            k.edge = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, eoffb, 0, 0));
+            return;
+        }
         const float *p = x + (n * C + ci) * plane + (int64_t)ih0 * W + col;
 #pragma unroll
         for (int i = 0; i < G::RPT; ++i) {
@@ -244,19 +288,6 @@ __device__ __forceinline__ void acc_init(floatx4 (&acc)[MB][R], const float *bs)
 }
 
 // ----------------------------------------------------------------- persistent kernel
-// Output stores through a buffer resource: a lane whose output lies outside the tensor gets
-// an offset past the resource's range, which the hardware drops.  Every tile thus issues the
-// same number of store instructions on every path, and the compiler can wait for the next
-// tile's prefetched loads (issued before these stores) without waiting for the stores.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kDropOffset = 0x80000000;  // >= kBufRange: the access is dropped
-constexpr int kBufRange = 0x7fffffff;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(float *base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kBufRange, kBufferWord3);
-}
-
 // Store one wave's R x 16 outputs of output channels [obase, obase + ocnt): tb points at
 // (n, obase, row h0, column 0); the wave's rows start at h0 + hrow0, its columns at wcol0.
 // Byte offsets from tb stay below 2^31 (checked by the host).
@@ -266,7 +297,7 @@ __device__ __forceinline__ void dw_epilogue_buf(float *tb, const DwsepDims &d, i
                                                 const floatx4 (&acc)[MB][R])
 {
     const int lane = threadIdx.x & 63;
-    const __amdgpu_buffer_rsrc_t rs = store_rsrc(tb);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tb);
     int plane = (int)(d.Ho * d.Wo);  // < 2^25 here
     int wo = (int)d.Wo;
     // Opaque to the optimiser: keeps the per-store offsets and lane masks from being hoisted
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
         [](int e) { return e; });
     if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
 
-    DwHaloStager<R, WH, VEC> hs;
+    DwHaloStager<R, WH, VEC, true> hs;
     hs.init(tid, d.pad);
     // lane bases: halo (pixel column 16*ww + j, rows R*wh ..; tap kw reads LDS column
     // 16*ww + j + kw + 4 - pad), pointwise fragments, depthwise taps of channel lane/16
@@ -392,14 +423,15 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     const float *pl = pwall + lane * MB;
     const float *dl = dkall + (lane >> 4) * 12;
 
+    // tile counts are below 2^31 (checked by the host): 32-bit index arithmetic
     auto decode = [&](int64_t tile, int64_t &n, int &h0, int &w0) {
-        int64_t t = xcd_tile(tile, tiles);
-        const int tw = (int)(t % tiles_w);
-        t /= tiles_w;
-        const int th = (int)(t % tiles_h);
-        n = t / tiles_h;
-        h0 = th * G::TH;
-        w0 = tw * kDwTW;
+        uint32_t t = (uint32_t)xcd_tile(tile, tiles);
+        const uint32_t tw = t % (uint32_t)tiles_w;
+        t /= (uint32_t)tiles_w;
+        const uint32_t th = t % (uint32_t)tiles_h;
+        n = t / (uint32_t)tiles_h;
+        h0 = (int)th * G::TH;
+        w0 = (int)tw * kDwTW;
     };
 
     // Per chunk: load the next chunk (after the last one, chunk 0 of the next tile) into
@@ -488,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const int64_t n = t / tiles_h;
     const int h0 = th * R, w0 = tw * kDwTW;
 
-    DwHaloStager<R, 1, VEC> hs;
+    DwHaloStager<R, 1, VEC, false> hs;
     hs.init(tid, d.pad);
     auto wload = [&](WC &wc, int c0) {
 #pragma unroll
@@ -627,8 +659,10 @@ hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, co
     // two 4-wave workgroups per CU, else one 8-wave workgroup, else the chunked kernel
     const size_t lds1 = wbytes + 4 * (size_t)DwGeom<R, 1>::XS;
     const size_t lds2 = wbytes + 4 * (size_t)DwGeom<R, 2>::XS;
-    // the persistent kernel addresses one tile's outputs with 32-bit byte offsets
-    const bool small_planes = 64 * MB * d.Ho * d.Wo <= kBufRange;
+    // the persistent kernel addresses one tile's outputs and one input image with 32-bit
+    // byte offsets
+    const bool small_planes =
+        64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
     if (small_planes && 2 * lds1 <= kLdsBytes)
         return launch_persistent<MB, R, 1, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase,
                                                          lds1, 2, s);
