@@ -130,6 +130,85 @@ struct HaloRows {
     }
 };
 
+// Buffer-resource access.  An offset at or past the resource's range is dropped by the
+// hardware (loads return 0, stores write nothing), so padding and ragged edges need no
+// branches, and a tile issues the same memory instructions on every path.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit access
+constexpr int kDropOffset = 0x80000000;   // >= kBufRange: the access is dropped
+constexpr int kBufRange = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, kBufRange,
+                                             kBufferWord3);
+}
+
+// HaloRows through a buffer resource: roff(row) is the byte offset of the row's column 0
+// from the resource base, or a negative value for an all-zero row (byte offsets of present
+// columns stay below 2^31).  Absent rows and columns outside [0, W) read as zero without
+// branches.
+template <int ROWS, int MAIN, int NT, bool VEC>
+struct BufHaloRows {
+    static constexpr int TPR = MAIN / 4;
+    static constexpr int RPP = NT / TPR;
+    static constexpr int P = (ROWS + RPP - 1) / RPP;
+    static constexpr int PE = (2 * ROWS + NT - 1) / NT;
+    static_assert(MAIN % 4 == 0 && NT % TPR == 0, "row split");
+    floatx4 m[P];
+    float e[PE];
+
+    template <class Roff>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, const Roff &roff, int col0,
+                                         int pad, int W)
+    {
+        const int t = threadIdx.x;
+        const int c = col0 + 4 * (t % TPR);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int row = t / TPR + p * RPP;
+            const int ro = row < ROWS ? roff(row) : -1;
+            if constexpr (VEC) {
+                const int off = ro >= 0 && c < W ? ro + 4 * c : kDropOffset;
+                m[p] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int off = ro >= 0 && c + i < W ? ro + 4 * (c + i) : kDropOffset;
+                    m[p][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int idx = t + p * NT;
+            const int row = idx >> 1, j = idx & 1;
+            const int ro = row < ROWS ? roff(row) : -1;
+            const int col = j < pad ? col0 - pad + j : col0 + MAIN + j - pad;
+            const int off = ro >= 0 && (unsigned)col < (unsigned)W ? ro + 4 * col : kDropOffset;
+            e[p] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        }
+    }
+
+    template <class Dst>
+    __device__ __forceinline__ void store(const Dst &dst, int pad) const
+    {
+        const int t = threadIdx.x;
+        const int q = t % TPR;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int row = t / TPR + p * RPP;
+            if (row < ROWS) *reinterpret_cast<floatx4 *>(dst(row) + 4 + 4 * q) = m[p];
+        }
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int idx = t + p * NT;
+            const int row = idx >> 1, j = idx & 1;
+            if (row < ROWS) dst(row)[j < pad ? 4 - pad + j : 4 + MAIN + j - pad] = e[p];
+        }
+    }
+};
+
 }  // namespace convfuse
 
 namespace convfuse {

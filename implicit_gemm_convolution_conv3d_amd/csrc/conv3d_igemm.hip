@@ -16,6 +16,8 @@
 // weights (in A-fragment order, [tap][channel group][lane][MB]) are staged into LDS one
 // chunk of CC input channels at a time; the next chunk's global loads are issued into
 // registers before the current chunk's MFMAs, so their latency hides behind the math.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,27 +42,48 @@ __device__ __forceinline__ float mish_tanh(float v)
 }
 
 // Weights of output channels [o0, o0 + 16*MB) x input channels [c0, c0 + CC), all 27 taps,
-// held in registers between the global load and the LDS store.  Thread t owns the
-// (channel, input channel) pairs t, t + NT, ...; its 27 taps are contiguous in memory.
+// held in registers between the global load and the LDS store.
 // LDS layout (A-fragment order): ws[((tap*CC/4 + cg)*64 + lane)*MB + mb] holds
 // w[o0 + 16*mb + lane%16][c0 + 4*cg + lane/16][tap].  Missing channels are zero.
+// Pair p = (cl*16 + j)*MB + mb names output channel 16*mb + j and input channel cl; its slot
+// at tap t is t*(CC/4)*64*MB + p, so threads holding consecutive pairs write consecutive LDS
+// words.  A pair's 27 taps are contiguous in memory.  With at least as many pairs as
+// threads, thread t owns the pairs t, t + NT, ...; with fewer, pair t % PAIRS is split over
+// TPP threads, TPT taps each.
 template <int MB, int CC, int NT>
 struct WeightChunk {
     static constexpr int PAIRS = 16 * MB * CC;
-    static constexpr int PP = (PAIRS + NT - 1) / NT;
-    float v[PP][27];
+    static constexpr int TPP = PAIRS >= NT ? 1 : NT / PAIRS;  // threads per pair
+    static constexpr int TPT = (27 + TPP - 1) / TPP;          // taps per thread
+    static constexpr int PP = (PAIRS * TPP + NT - 1) / NT;
+    static constexpr int TAPSTRIDE = (CC / 4) * 64 * MB;
+    static_assert(PAIRS >= NT || NT % PAIRS == 0, "pair split");
+    float v[PP][TPT];
+
+    __device__ __forceinline__ static void decode(int idx, int &pair, int &t0)
+    {
+        if constexpr (TPP == 1) {
+            pair = idx;
+            t0 = 0;
+        } else {
+            pair = idx % PAIRS;
+            t0 = (idx / PAIRS) * TPT;
+        }
+    }
 
     __device__ __forceinline__ void load(const float *__restrict__ w, const Conv3dDims &d, int o0,
                                          int c0)
     {
 #pragma unroll
         for (int p = 0; p < PP; ++p) {
-            const int pair = threadIdx.x + p * NT;
-            const int o = o0 + pair / CC, c = c0 + pair % CC;
+            int pair, t0;
+            decode(threadIdx.x + p * NT, pair, t0);
+            const int mb = pair % MB, jj = (pair / MB) % 16, cl = pair / (16 * MB);
+            const int o = o0 + 16 * mb + jj, c = c0 + cl;
             const bool ok = pair < PAIRS && o < d.O && c < d.C;
-            const float *src = w + ((int64_t)o * d.C + c) * 27;
+            const float *src = w + ((int64_t)o * d.C + c) * 27 + t0;
 #pragma unroll
-            for (int tap = 0; tap < 27; ++tap) v[p][tap] = ok ? src[tap] : 0.0f;
+            for (int i = 0; i < TPT; ++i) v[p][i] = ok && t0 + i < 27 ? src[i] : 0.0f;
         }
     }
 
@@ -68,12 +91,12 @@ struct WeightChunk {
     {
 #pragma unroll
         for (int p = 0; p < PP; ++p) {
-            const int pair = threadIdx.x + p * NT;
+            int pair, t0;
+            decode(threadIdx.x + p * NT, pair, t0);
             if (pair >= PAIRS) continue;
-            const int ol = pair / CC, cl = pair % CC;
-            const int base = ((cl >> 2) * 64 + (cl & 3) * 16 + (ol & 15)) * MB + (ol >> 4);
 #pragma unroll
-            for (int tap = 0; tap < 27; ++tap) ws[tap * (CC / 4) * 64 * MB + base] = v[p][tap];
+            for (int i = 0; i < TPT; ++i)
+                if (t0 + i < 27) ws[(t0 + i) * TAPSTRIDE + pair] = v[p][i];
         }
     }
 };
@@ -129,25 +152,43 @@ __device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
 }
 
 // Staging of one chunk for a workgroup whose input box is [id0, id0+HD) x [ih0, ih0+HH) x
-// columns [iw0 - pad, iw0 - pad + MAIN + 2), plus its weights.
-template <int MB, int CC, int HD, int HH, int MAIN, int RS, int CS, int NT, bool VEC>
+// columns [iw0 - pad, iw0 - pad + MAIN + 2), plus its weights.  BUF: the halo is read
+// through a buffer resource over the chunk's CC input channels of image n (their byte size
+// below 2^31), with 32-bit row offsets and dropped offsets for the padding; otherwise
+// through plain loads with a branch per row.
+template <int MB, int CC, int HD, int HH, int MAIN, int RS, int CS, int NT, bool VEC, bool BUF>
 struct ChunkStage {
-    HaloRows<CC * HD * HH, MAIN, NT, VEC> halo;
+    using Halo = std::conditional_t<BUF, BufHaloRows<CC * HD * HH, MAIN, NT, VEC>,
+                                    HaloRows<CC * HD * HH, MAIN, NT, VEC>>;
+    Halo halo;
     WeightChunk<MB, CC, NT> wts;
 
     __device__ __forceinline__ void load(const float *__restrict__ x, const float *__restrict__ w,
                                          const Conv3dDims &d, int64_t n, int c0, int o0, int id0,
                                          int ih0, int iw0)
     {
-        auto src = [&](int row) -> const float * {
-            const int hh = row % HH, t = row / HH;
-            const int hd = t % HD, c = t / HD;
-            const int ci = c0 + c, id = id0 + hd, ih = ih0 + hh;
-            if (ci >= d.C || (unsigned)id >= (unsigned)d.D || (unsigned)ih >= (unsigned)d.H)
-                return nullptr;
-            return x + (((n * d.C + ci) * d.D + id) * d.H + ih) * d.W;
-        };
-        halo.load(src, iw0, d.pad, (int)d.W);
+        if constexpr (BUF) {
+            const int D = (int)d.D, H = (int)d.H, W = (int)d.W, cn = (int)(d.C - c0);
+            auto roff = [&](int row) -> int {
+                const int hh = row % HH, t = row / HH;
+                const int hd = t % HD, c = t / HD;
+                const int id = id0 + hd, ih = ih0 + hh;
+                if (c >= cn || (unsigned)id >= (unsigned)D || (unsigned)ih >= (unsigned)H)
+                    return -1;
+                return 4 * (((c * D + id) * H + ih) * W);
+            };
+            halo.load(buffer_rsrc(x + (n * d.C + c0) * d.D * d.H * d.W), roff, iw0, d.pad, W);
+        } else {
+            auto src = [&](int row) -> const float * {
+                const int hh = row % HH, t = row / HH;
+                const int hd = t % HD, c = t / HD;
+                const int ci = c0 + c, id = id0 + hd, ih = ih0 + hh;
+                if (ci >= d.C || (unsigned)id >= (unsigned)d.D || (unsigned)ih >= (unsigned)d.H)
+                    return nullptr;
+                return x + (((n * d.C + ci) * d.D + id) * d.H + ih) * d.W;
+            };
+            halo.load(src, iw0, d.pad, (int)d.W);
+        }
         wts.load(w, d, o0, c0);
     }
 
@@ -166,7 +207,7 @@ struct ChunkStage {
 
 // ------------------------------------------------------------------ Mish/tanh epilogue
 // Wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns [ow0, ow0 + 16*NBW).
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC>
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
 __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
@@ -198,7 +239,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) boff[nb] = 16 * nb;
 
-    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC> stage;
+    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC, BUF> stage;
     const int id0 = od0 - d.pad, ih0 = oh0 - d.pad;
     stage.load(x, w, d, n, 0, o0, id0, ih0, ow0);
 
@@ -246,7 +287,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
 // voxel blocks are (dd, dh, q): conv voxel (2pd + dd, 2ph + dh, 2pw0 + 16q + j) for lane
 // column j, so the max over (dd, dh) is taken inside a lane and the max over the window's
 // two columns between lanes j and j^1.
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool PREFETCH>
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool PREFETCH>
 __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     float *__restrict__ out, PoolDims pd_, int64_t tiles, int tiles_w, int tiles_h,
@@ -286,7 +327,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
             for (int q = 0; q < NBW; ++q)
                 boff[(dd * 2 + dh) * NBW + q] = (dd * HH + dh) * RS + 16 * q;
 
-    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC> stage;
+    ChunkStage<MB, CC, HD, HH, MAIN, RS, CS, NT, VEC, BUF> stage;
     auto next = [&](int c0) {
         // With PREFETCH the chunk after c0 is loaded into registers while c0 computes;
         // without it each chunk is loaded right before it is stored, and other resident
@@ -376,6 +417,19 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline bool vec_ok(const float *x, int64_t W) { return W % 4 == 0 && ((uintptr_t)x & 15) == 0; }
 
+// 32-bit byte offsets over one staged chunk of CC input channels
+inline bool buf_ok(const Conv3dDims &d, int CC) { return 4 * CC * d.D * d.H * d.W <= kBufRange; }
+
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
+void launch_act_kernel(const float *x, const float *w, const float *b, float *y,
+                       const Conv3dDims &d, int64_t tiles, int64_t tw, int64_t th, int64_t td,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF>),
+                       dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
+                       (int)tw, (int)th, (int)td);
+}
+
 template <int MB, int NBW, int WD, int WH, int CC>
 hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
                       const Conv3dDims &d, hipStream_t s)
@@ -384,15 +438,22 @@ hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
     const int64_t og = cdiv(d.O, 16 * MB);
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (vec_ok(x, d.W))
-        hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, true>),
-                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
-                           (int)tw, (int)th, (int)td);
-    else
-        hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, false>),
-                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
-                           (int)tw, (int)th, (int)td);
+    const bool v = vec_ok(x, d.W), bf = buf_ok(d, CC);
+    if (v && bf) launch_act_kernel<MB, NBW, WD, WH, CC, true, true>(x, w, b, y, d, tiles, tw, th, td, s);
+    else if (v) launch_act_kernel<MB, NBW, WD, WH, CC, true, false>(x, w, b, y, d, tiles, tw, th, td, s);
+    else if (bf) launch_act_kernel<MB, NBW, WD, WH, CC, false, true>(x, w, b, y, d, tiles, tw, th, td, s);
+    else launch_act_kernel<MB, NBW, WD, WH, CC, false, false>(x, w, b, y, d, tiles, tw, th, td, s);
     return hipGetLastError();
+}
+
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
+void launch_pool_kernel(const float *x, const float *w, const float *conv_b, float *out,
+                        const PoolDims &p, int64_t tiles, int64_t tw, int64_t th, int64_t td,
+                        float inv_count, hipStream_t s)
+{
+    hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, VEC, BUF, BUF>),
+                       dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
+                       tiles, (int)tw, (int)th, (int)td, inv_count);
 }
 
 }  // namespace
@@ -424,14 +485,11 @@ hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *c
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
-    if (vec_ok(x, d.W))
-        hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, true, false>),
-                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
-                           tiles, (int)tw, (int)th, (int)td, inv_count);
-    else
-        hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, false, false>),
-                           dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
-                           tiles, (int)tw, (int)th, (int)td, inv_count);
+    const bool v = vec_ok(x, d.W), bf = buf_ok(d, CC);
+    if (v && bf) launch_pool_kernel<MB, NBW, WD, WH, CC, true, true>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else if (v) launch_pool_kernel<MB, NBW, WD, WH, CC, true, false>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else if (bf) launch_pool_kernel<MB, NBW, WD, WH, CC, false, true>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else launch_pool_kernel<MB, NBW, WD, WH, CC, false, false>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
     return hipGetLastError();
 }
 

@@ -37,21 +37,7 @@ namespace convfuse {
 namespace {
 
 constexpr int kDwCC = 16;  // input channels per chunk
-constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit access
 constexpr int kDwTW = 64;  // output tile width (4 waves x 16 columns)
-
-// Buffer-resource access.  An offset at or past the resource's range is dropped by the
-// hardware (loads return 0, stores write nothing), so padding and ragged edges need no
-// branches, and a tile issues the same memory instructions on every path.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kDropOffset = 0x80000000;  // >= kBufRange: the access is dropped
-constexpr int kBufRange = 0x7fffffff;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, kBufRange,
-                                             kBufferWord3);
-}
 
 template <int R, int WH>
 struct DwGeom {
