@@ -39,54 +39,64 @@ namespace {
 constexpr int kDwCC = 16;  // input channels per chunk
 constexpr int kDwTW = 64;  // output tile width (4 waves x 16 columns)
 
-template <int R, int WH>
+// Tile geometry: 4*WH waves, R output rows per wave, tile 64 columns x R*WH rows; CC input
+// channels per chunk.  Staging threads: (channel, column quad) pairs fill 16*CC threads; the
+// remaining factor RG splits the halo rows.
+template <int R, int WH, int CC>
 struct DwGeom {
     static constexpr int NWAVE = 4 * WH;
     static constexpr int NT = 64 * NWAVE;
     static constexpr int TH = R * WH;                  // output tile rows
     static constexpr int HR = TH + 2;                  // halo rows
-    static_assert(HR % WH == 0, "halo rows split evenly over the row groups");
-    static constexpr int RPT = HR / WH;                // halo rows per staging thread
+    static_assert(NT % (16 * CC) == 0, "whole (channel, quad) groups");
+    static constexpr int RG = NT / (16 * CC);          // row groups
+    static_assert(HR % RG == 0, "halo rows split evenly over the row groups");
+    static constexpr int RPT = HR / RG;                // halo rows per staging thread
     static constexpr int RS = kDwTW + 8;               // LDS row: 4 + 64 columns + edges
     static constexpr int CS = halo_channel_stride(HR * RS);
-    static constexpr int XS = kDwCC * CS;              // one chunk of halo
-    static constexpr int EDGES = 2 * kDwCC * HR;       // edge values per chunk
-    static_assert(EDGES <= NT, "one edge value per thread");
+    static constexpr int XS = CC * CS;                 // one chunk of halo
+    static constexpr int EDGES = 2 * CC * HR;          // edge values per chunk
+    static constexpr int PE = (EDGES + NT - 1) / NT;   // edge values per thread
 };
 
 // Halo rows of one chunk held in registers between global load and LDS store.
-template <int R, int WH>
+template <int R, int WH, int CC>
 struct DwHalo {
-    floatx4 xr[DwGeom<R, WH>::RPT];
-    float edge;
+    floatx4 xr[DwGeom<R, WH, CC>::RPT];
+    float edge[DwGeom<R, WH, CC>::PE];
 };
 
 // Load (registers) and store (LDS) of one chunk of the halo of tile (n, h0, w0).  Thread t:
-// channel sc = (t/16)%16, column quad sq = t%16, halo rows rg*RPT .. +RPT-1 (rg = t/256);
-// edge value: thread e < EDGES takes the column left of w0 or right of w0+63 of row
-// (e/(2HR), (e%(2HR))/2).  LDS row layout: column 4 + j holds global column w0 + j.
+// channel sc = (t/16)%CC, column quad sq = t%16, halo rows rg*RPT .. +RPT-1 (rg = t/(16CC));
+// edge value e = t + p*NT (< EDGES) is the column left of w0 or right of w0+63 of channel
+// e/(2HR), halo row (e%(2HR))/2.  LDS row layout: column 4 + j holds global column w0 + j.
 // BUF: loads through a buffer resource over image n (its byte size below 2^31), with
 // dropped offsets for the zero padding, instead of branches around plain loads.
-template <int R, int WH, bool VEC, bool BUF>
+template <int R, int WH, int CC, bool VEC, bool BUF>
 struct DwHaloStager {
-    using G = DwGeom<R, WH>;
-    int sc, sq, rg, ec, ehr, eoff;
+    using G = DwGeom<R, WH, CC>;
+    int sc, sq, rg;
+    int ec[G::PE], ehr[G::PE], eoff[G::PE];
 
     __device__ __forceinline__ void init(int tid, int pad)
     {
-        sc = (tid >> 4) & 15;
+        sc = (tid >> 4) % CC;
         sq = tid & 15;
-        rg = tid >> 8;
-        ec = tid / (2 * G::HR);
-        const int erem = tid % (2 * G::HR);
-        ehr = erem >> 1;
-        const int ej = erem & 1;
-        eoff = ej < pad ? -pad + ej : kDwTW + ej - pad;  // edge column - w0
+        rg = tid / (16 * CC);
+#pragma unroll
+        for (int p = 0; p < G::PE; ++p) {
+            const int e = tid + p * G::NT;
+            ec[p] = e < G::EDGES ? e / (2 * G::HR) : CC;  // CC: no edge value
+            const int erem = e % (2 * G::HR);
+            ehr[p] = erem >> 1;
+            const int ej = erem & 1;
+            eoff[p] = ej < pad ? -pad + ej : kDwTW + ej - pad;  // edge column - w0
+        }
     }
 
-    __device__ __forceinline__ void load(DwHalo<R, WH> &k, const float *__restrict__ x,
-                                         const DwsepDims &d, int64_t n, int h0, int w0, int c0,
-                                         int tid) const
+    __device__ __forceinline__ void load(DwHalo<R, WH, CC> &k, const float *__restrict__ x,
+                                         const DwsepDims &d, int64_t n, int h0, int w0,
+                                         int c0) const
     {
         const int C = (int)d.C, H = (int)d.H, W = (int)d.W;
         const int64_t plane = (int64_t)H * W;
@@ -115,11 +125,15 @@ struct DwHaloStager {
                     }
                 }
             }
-            const int eci = c0 + ec, eih = ih0 + ehr, ecol = w0 + eoff;
-            const bool eok = tid < G::EDGES && eci < C && (unsigned)eih < (unsigned)H &&
-                             (unsigned)ecol < (unsigned)W;
-            const int eoffb = eok ? 4 * (((eci < C ? eci : 0) * H + eih) * W + ecol) : kDropOffset;
-            k.edge = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, eoffb, 0, 0));
+#pragma unroll
+            for (int p = 0; p < G::PE; ++p) {
+                const int eci = c0 + ec[p], eih = ih0 + ehr[p], ecol = w0 + eoff[p];
+                const bool eok = ec[p] < CC && eci < C && (unsigned)eih < (unsigned)H &&
+                                 (unsigned)ecol < (unsigned)W;
+                const int eoffb =
+                    eok ? 4 * (((eci < C ? eci : 0) * H + eih) * W + ecol) : kDropOffset;
+                k.edge[p] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, eoffb, 0, 0));
+            }
             return;
         }
         const float *p = x + (n * C + ci) * plane + (int64_t)ih0 * W + col;
@@ -139,19 +153,24 @@ struct DwHaloStager {
             }
             k.xr[i] = v;
         }
-        const int eci = c0 + ec, eih = ih0 + ehr, ecol = w0 + eoff;
-        float e = 0.0f;
-        if (tid < G::EDGES && eci < C && (unsigned)eih < (unsigned)H && (unsigned)ecol < (unsigned)W)
-            e = x[((n * C + eci) * H + eih) * (int64_t)W + ecol];
-        k.edge = e;
+#pragma unroll
+        for (int q = 0; q < G::PE; ++q) {
+            const int eci = c0 + ec[q], eih = ih0 + ehr[q], ecol = w0 + eoff[q];
+            float e = 0.0f;
+            if (ec[q] < CC && eci < C && (unsigned)eih < (unsigned)H && (unsigned)ecol < (unsigned)W)
+                e = x[((n * C + eci) * H + eih) * (int64_t)W + ecol];
+            k.edge[q] = e;
+        }
     }
 
-    __device__ __forceinline__ void store(float *xs, const DwHalo<R, WH> &k, int tid) const
+    __device__ __forceinline__ void store(float *xs, const DwHalo<R, WH, CC> &k) const
     {
         float *row = xs + sc * G::CS + rg * G::RPT * G::RS + 4 + 4 * sq;
 #pragma unroll
         for (int i = 0; i < G::RPT; ++i) *reinterpret_cast<floatx4 *>(row + i * G::RS) = k.xr[i];
-        if (tid < G::EDGES) xs[ec * G::CS + ehr * G::RS + 4 + eoff] = k.edge;
+#pragma unroll
+        for (int p = 0; p < G::PE; ++p)
+            if (ec[p] < CC) xs[ec[p] * G::CS + ehr[p] * G::RS + 4 + eoff[p]] = k.edge[p];
     }
 };
 
@@ -159,12 +178,12 @@ struct DwHaloStager {
 // pointwise weights of the chunk's first k-step, lane base applied (pw[cg*64*MB + mb] is the
 // operand of k-step cg, output block mb); dk: depthwise taps [c][12] (9 taps, bias at 9) of
 // the chunk's channel 4*cg + lane/16 at dk[cg*48].
-template <int MB, int R, int RS, int CS, bool PIXROWS>
+template <int MB, int R, int RS, int CS, int CC, bool PIXROWS>
 __device__ __forceinline__ void dw_chunk(const float *xs, const float *pw, const float *dk,
                                          floatx4 (&acc)[MB][R])
 {
 #pragma unroll
-    for (int cg = 0; cg < kDwCC / 4; ++cg) {
+    for (int cg = 0; cg < CC / 4; ++cg) {
         const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg);
         const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 4);
         const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 8);
@@ -347,25 +366,25 @@ __device__ __forceinline__ void lds_fill(float *dst, int total, const V &value, 
 }
 
 // Dynamic LDS: [halo chunk XS][pointwise fragments KS*64*MB][depthwise taps 4*KS*12]
-// [pointwise bias 16*MB], KS = 4*ceil(C/16) k-steps (whole chunks; zero past C).  Fragment
+// [pointwise bias 16*MB], KS = (CC/4)*ceil(C/CC) k-steps (whole chunks; zero past C).  Fragment
 // order: pwall[(s*64 + lane)*MB + mb] = pw_w[obase + 16*mb + lane%16][4*s + lane/16].
-template <int MB>
+template <int MB, int CC>
 constexpr size_t dw_weight_floats(int64_t C)
 {
-    const int64_t KS = (C + kDwCC - 1) / kDwCC * (kDwCC / 4);
+    const int64_t KS = (C + CC - 1) / CC * (CC / 4);
     return (size_t)(KS * 64 * MB + 4 * KS * 12 + 16 * MB);
 }
 
-template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS>
 __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
     DwsepDims d, int obase, int64_t tiles, int tiles_w, int tiles_h)
 {
-    using G = DwGeom<R, WH>;
+    using G = DwGeom<R, WH, CC>;
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     const int C = (int)d.C;  // small: the weights fit in LDS
-    const int KS = (C + kDwCC - 1) / kDwCC * (kDwCC / 4);
+    const int KS = (C + CC - 1) / CC * (CC / 4);
     float *xs = dyn;
     float *pwall = dyn + G::XS;
     float *dkall = pwall + KS * 64 * MB;
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
         [](int e) { return e; });
     if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
 
-    DwHaloStager<R, WH, VEC, true> hs;
+    DwHaloStager<R, WH, CC, VEC, true> hs;
     hs.init(tid, d.pad);
     // lane bases: halo (pixel column 16*ww + j, rows R*wh ..; tap kw reads LDS column
     // 16*ww + j + kw + 4 - pad), pointwise fragments, depthwise taps of channel lane/16
@@ -427,10 +446,10 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     int64_t tile = blockIdx.x, n;
     int h0, w0;
     decode(tile, n, h0, w0);
-    DwHalo<R, WH> k;
-    hs.load(k, x, d, n, h0, w0, 0, tid);
+    DwHalo<R, WH, CC> k;
+    hs.load(k, x, d, n, h0, w0, 0);
     lds_barrier();  // weights written; no wave reads the halo buffer yet
-    hs.store(xs, k, tid);
+    hs.store(xs, k);
     lds_barrier();
     floatx4 acc[MB][R];
     for (;;) {
@@ -438,10 +457,10 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
         const int64_t ntile = tile + gridDim.x;
         int64_t nn = 0;
         int nh0 = 0, nw0 = 0;
-        for (int c0 = 0;; c0 += kDwCC) {
-            const bool last = c0 + kDwCC >= C;
+        for (int c0 = 0;; c0 += CC) {
+            const bool last = c0 + CC >= C;
             int64_t ln = n;
-            int lh = h0, lw = w0, lc = c0 + kDwCC;
+            int lh = h0, lw = w0, lc = c0 + CC;
             if (last) {
                 if (ntile < tiles) decode(ntile, nn, nh0, nw0);
                 ln = nn;
@@ -449,11 +468,12 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
                 lw = nw0;
                 lc = 0;
             }
-            if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc, tid);
-            dw_chunk<MB, R, G::RS, G::CS, PIXROWS>(xl, pl + (c0 / 4) * 64 * MB, dl + c0 * 12, acc);
+            if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc);
+            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS>(xl, pl + (c0 / 4) * 64 * MB, dl + c0 * 12,
+                                                       acc);
             if (last) break;
             lds_barrier();
-            hs.store(xs, k, tid);
+            hs.store(xs, k);
             lds_barrier();
         }
         float *tb = y + ((n * d.O + obase) * d.Ho + h0) * d.Wo;
@@ -465,7 +485,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
         h0 = nh0;
         w0 = nw0;
         lds_barrier();
-        hs.store(xs, k, tid);
+        hs.store(xs, k);
         lds_barrier();
     }
 }
@@ -487,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
     DwsepDims d, int obase, int64_t tiles, int tiles_w, int tiles_h)
 {
-    using G = DwGeom<R, 1>;
+    using G = DwGeom<R, 1, kDwCC>;
     using WC = DwWeightChunk<MB>;
     constexpr int PS = kDwCC * 16 * MB, DS = kDwCC * 12;
     __shared__ __attribute__((aligned(16))) float lds[G::XS + PS + DS + 16 * MB];
@@ -506,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const int64_t n = t / tiles_h;
     const int h0 = th * R, w0 = tw * kDwTW;
 
-    DwHaloStager<R, 1, VEC, false> hs;
+    DwHaloStager<R, 1, kDwCC, VEC, false> hs;
     hs.init(tid, d.pad);
     auto wload = [&](WC &wc, int c0) {
 #pragma unroll
@@ -551,35 +571,35 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const float *dl = ds + (lane >> 4) * 12;
     const bool active = w0 + 16 * wave < d.Wo;
 
-    DwHalo<R, 1> k;
+    DwHalo<R, 1, kDwCC> k;
     WC wc;
-    hs.load(k, x, d, n, h0, w0, 0, tid);
+    hs.load(k, x, d, n, h0, w0, 0);
     wload(wc, 0);
     if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
     if (active) {
         floatx4 acc[MB][R];
         for (int c0 = 0; c0 < C; c0 += kDwCC) {
             lds_barrier();
-            hs.store(xs, k, tid);
+            hs.store(xs, k);
             wstore(wc);
             lds_barrier();
             if (c0 == 0) acc_init<MB, R, PIXROWS>(acc, bs);
             if (c0 + kDwCC < C) {
-                hs.load(k, x, d, n, h0, w0, c0 + kDwCC, tid);
+                hs.load(k, x, d, n, h0, w0, c0 + kDwCC);
                 wload(wc, c0 + kDwCC);
             }
-            dw_chunk<MB, R, G::RS, G::CS, PIXROWS>(xl, pl, dl, acc);
+            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS>(xl, pl, dl, acc);
         }
         dw_epilogue<MB, R, PIXROWS>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
     } else {
         // This wave's columns lie past the output: it only helps stage the shared tiles.
         for (int c0 = 0; c0 < C; c0 += kDwCC) {
             lds_barrier();
-            hs.store(xs, k, tid);
+            hs.store(xs, k);
             wstore(wc);
             lds_barrier();
             if (c0 + kDwCC < C) {
-                hs.load(k, x, d, n, h0, w0, c0 + kDwCC, tid);
+                hs.load(k, x, d, n, h0, w0, c0 + kDwCC);
                 wload(wc, c0 + kDwCC);
             }
         }
@@ -600,13 +620,13 @@ int cu_count()
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS>
 hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_b,
                              const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
                              int obase, size_t lds, int per_cu, hipStream_t s)
 {
-    using G = DwGeom<R, WH>;
-    auto kern = dwsep_persistent_kernel<MB, R, WH, VEC, PIXROWS>;
+    using G = DwGeom<R, WH, CC>;
+    auto kern = dwsep_persistent_kernel<MB, R, WH, CC, VEC, PIXROWS>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -636,25 +656,30 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
     return hipGetLastError();
 }
 
-// Pick the kernel for output channels [obase, obase + min(16*MB, O - obase)).
+// Pick the kernel for output channels [obase, obase + min(16*MB, O - obase)): the persistent
+// kernel with one 8-wave workgroup per CU and 32-channel chunks when its weights and halo fit
+// in LDS, else with 16-channel chunks (two 4-wave workgroups per CU, or one 8-wave one), else
+// the chunked kernel.
 template <int MB, int R, bool VEC, bool PIXROWS>
 hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                         const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
-    const size_t wbytes = 4 * dw_weight_floats<MB>(d.C);
-    // two 4-wave workgroups per CU, else one 8-wave workgroup, else the chunked kernel
-    const size_t lds1 = wbytes + 4 * (size_t)DwGeom<R, 1>::XS;
-    const size_t lds2 = wbytes + 4 * (size_t)DwGeom<R, 2>::XS;
+    const size_t lds_a = 4 * (dw_weight_floats<MB, 32>(d.C) + (size_t)DwGeom<R, 2, 32>::XS);
+    const size_t lds_b = 4 * (dw_weight_floats<MB, 16>(d.C) + (size_t)DwGeom<R, 1, 16>::XS);
+    const size_t lds_c = 4 * (dw_weight_floats<MB, 16>(d.C) + (size_t)DwGeom<R, 2, 16>::XS);
     // the persistent kernel addresses one tile's outputs and one input image with 32-bit
     // byte offsets
     const bool small_planes =
         64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
-    if (small_planes && 2 * lds1 <= kLdsBytes)
-        return launch_persistent<MB, R, 1, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase,
-                                                         lds1, 2, s);
-    if (small_planes && lds2 <= kLdsBytes)
-        return launch_persistent<MB, R, 2, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase,
-                                                         lds2, 1, s);
+    if (small_planes && lds_a <= kLdsBytes)
+        return launch_persistent<MB, R, 2, 32, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+                                                             obase, lds_a, 1, s);
+    if (small_planes && 2 * lds_b <= kLdsBytes)
+        return launch_persistent<MB, R, 1, 16, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+                                                             obase, lds_b, 2, s);
+    if (small_planes && lds_c <= kLdsBytes)
+        return launch_persistent<MB, R, 2, 16, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+                                                             obase, lds_c, 1, s);
     return launch_chunked<MB, 2, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
 }
 
@@ -682,7 +707,7 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
     // One launch covers up to 192 output channels; wider layers run as several launches over
     // consecutive output-channel slices (each rereads the input).
     if (d.O <= 64) return launch<4, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
-    if (d.O <= 128) return launch<8, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
+    if (d.O <= 128) return launch<8, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
     for (int64_t o0 = 0; o0 < d.O; o0 += 192) {
         const hipError_t e = launch<12, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, (int)o0, s);
         if (e != hipSuccess) return e;
