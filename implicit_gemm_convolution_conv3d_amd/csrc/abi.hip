@@ -33,10 +33,22 @@ constexpr int64_t kMaxElems = 1LL << 60;
 bool out_len(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d, int64_t *out)
 {
     if (in <= 0 || k <= 0 || s <= 0 || p < 0 || d <= 0) return false;
-    if (in > kMaxDim || k > kMaxDim || p > kMaxDim || d > kMaxDim) return false;
+    if (in > kMaxDim || k > kMaxDim || s > kMaxDim || p > kMaxDim || d > kMaxDim) return false;
     const int64_t span = in + 2 * p - d * (k - 1) - 1;
     if (span < 0) return false;
     *out = span / s + 1;
+    return true;
+}
+
+// Taps of a k^dims kernel: the general kernels index them with 32-bit integers.
+constexpr int64_t kMaxTaps = 1LL << 30;
+bool taps_ok(int64_t k, int dims)
+{
+    int64_t t = 1;
+    for (int i = 0; i < dims; ++i) {
+        t *= k;
+        if (t > kMaxTaps) return false;
+    }
     return true;
 }
 
@@ -95,18 +107,23 @@ int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y, i
                     "output",
                     (long long)D, (long long)H, (long long)W, (long long)k, (long long)stride,
                     (long long)pad);
-    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}))
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}) ||
+        !elems_ok({Cout, Cin, k, k, k}))
         return fail(CONVFUSE_ERR_SHAPE, "conv3d_mish_tanh: tensor too large");
-    if (k != 3 || stride != 1 || pad > 2)
-        return fail(CONVFUSE_ERR_UNSUPPORTED,
-                    "conv3d_mish_tanh: GPU path implements k=3, stride=1, pad<=2 (got k=%lld "
-                    "stride=%lld pad=%lld)",
-                    (long long)k, (long long)stride, (long long)pad);
+    if (!taps_ok(k, 3))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "conv3d_mish_tanh: k=%lld: more than 2^30 taps",
+                    (long long)k);
     if (N == 0) return CONVFUSE_OK;
     if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "conv3d_mish_tanh: x, w and y are required");
     convfuse::Conv3dDims d{N, Cin, D, H, W, Cout, OD, OH, OW, (int)pad};
-    return device_status(convfuse::launch_conv3d_mish_tanh(x, w, b, y, d, (hipStream_t)stream),
-                         "conv3d_mish_tanh launch");
+    if (k == 3 && stride == 1 && pad <= 2)
+        return device_status(
+            convfuse::launch_conv3d_mish_tanh(x, w, b, y, d, (hipStream_t)stream),
+            "conv3d_mish_tanh launch");
+    const convfuse::GenConv g{(int)k, (int)stride, 1};
+    return device_status(
+        convfuse::launch_conv3d_mish_tanh_generic(x, w, b, y, d, g, (hipStream_t)stream),
+        "conv3d_mish_tanh launch");
 }
 
 int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
@@ -129,19 +146,27 @@ int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float 
         !out_len(OW, pool, pool, 0, 1, &PW) || PD <= 0 || PH <= 0 || PW <= 0)
         return fail(CONVFUSE_ERR_SHAPE, "%s: pool=%lld does not fit the %lldx%lldx%lld conv output",
                     fn, (long long)pool, (long long)OD, (long long)OH, (long long)OW);
-    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}))
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}) ||
+        !elems_ok({Cout, Cin, k, k, k}))
         return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
-    if (k != 3 || pool != 2)
-        return fail(CONVFUSE_ERR_UNSUPPORTED,
-                    "%s: GPU path implements k=3, pool=2 (got k=%lld pool=%lld)", fn,
-                    (long long)k, (long long)pool);
+    if (!taps_ok(k, 3))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: k=%lld: more than 2^30 taps", fn,
+                    (long long)k);
+    if (pool > convfuse::kGenericMaxPool)
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: GPU path implements pool<=%d (got pool=%lld)",
+                    fn, convfuse::kGenericMaxPool, (long long)pool);
     if (N == 0) return CONVFUSE_OK;
     if (!x || !w || !bias || !out)
         return fail(CONVFUSE_ERR_NULL, "%s: x, w, bias and out are required", fn);
     convfuse::PoolDims p{{N, Cin, D, H, W, Cout, OD, OH, OW, 0}, PD, PH, PW, divisor};
-    return device_status(
-        convfuse::launch_conv3d_pool_sum(x, w, conv_b, bias, out, p, (hipStream_t)stream),
-        "conv3d_div_maxpool_gap_bias_sum launch");
+    if (k == 3 && pool == 2)
+        return device_status(
+            convfuse::launch_conv3d_pool_sum(x, w, conv_b, bias, out, p, (hipStream_t)stream),
+            "conv3d_div_maxpool_gap_bias_sum launch");
+    const convfuse::GenConv g{(int)k, 1, 1};
+    return device_status(convfuse::launch_conv3d_pool_sum_generic(x, w, conv_b, bias, out, p, g,
+                                                                  (int)pool, (hipStream_t)stream),
+                         "conv3d_div_maxpool_gap_bias_sum launch");
 }
 
 int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
@@ -160,20 +185,23 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                     "no output",
                     (long long)H, (long long)W, (long long)K, (long long)stride, (long long)pad,
                     (long long)dilation);
-    if (!elems_ok({N, Cin, H, W}) || !elems_ok({N, Cout, Ho, Wo}))
+    if (!elems_ok({N, Cin, H, W}) || !elems_ok({N, Cout, Ho, Wo}) || !elems_ok({Cin, K, K}))
         return fail(CONVFUSE_ERR_SHAPE, "dwsep_conv2d: tensor too large");
-    if (K != 3 || stride != 1 || dilation != 1 || pad > 2)
-        return fail(CONVFUSE_ERR_UNSUPPORTED,
-                    "dwsep_conv2d: GPU path implements K=3, stride=1, dilation=1, pad<=2 (got "
-                    "K=%lld stride=%lld pad=%lld dilation=%lld)",
-                    (long long)K, (long long)stride, (long long)pad, (long long)dilation);
+    if (!taps_ok(K, 2))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "dwsep_conv2d: K=%lld: more than 2^30 taps",
+                    (long long)K);
     if (N == 0) return CONVFUSE_OK;
     if (!x || !dw_w || !pw_w || !y)
         return fail(CONVFUSE_ERR_NULL, "dwsep_conv2d: x, dw_w, pw_w and y are required");
     convfuse::DwsepDims d{N, Cin, H, W, Cout, Ho, Wo, (int)pad};
-    return device_status(
-        convfuse::launch_dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, y, d, (hipStream_t)stream),
-        "dwsep_conv2d launch");
+    if (K == 3 && stride == 1 && dilation == 1 && pad <= 2)
+        return device_status(
+            convfuse::launch_dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, y, d, (hipStream_t)stream),
+            "dwsep_conv2d launch");
+    const convfuse::GenConv g{(int)K, (int)stride, (int)dilation};
+    return device_status(convfuse::launch_dwsep_conv2d_generic(x, dw_w, dw_b, pw_w, pw_b, y, d, g,
+                                                               (hipStream_t)stream),
+                         "dwsep_conv2d launch");
 }
 
 }  // extern "C"

@@ -25,22 +25,6 @@ namespace convfuse {
 
 namespace {
 
-// tanh(mish(v)), mish(v) = v * tanh(softplus(v)), softplus(v) = v for v > 20 (PyTorch's
-// threshold).  For v <= 20, tanh(log(1 + e^v)) = n / (n + 2) with n = e^v (e^v + 2); for
-// v > 20, tanh(v) rounds to 1 in fp32, so mish(v) = v.  The outer tanh(m) = 1 - 2/(e^2m + 1);
-// m >= -0.31 keeps e^2m away from 0, and its overflow to +inf gives exactly 1.
-__device__ __forceinline__ float mish_tanh(float v)
-{
-    float t = 1.0f;
-    if (v <= 20.0f) {
-        const float e = __expf(v);
-        const float n = e * (e + 2.0f);
-        t = __fdividef(n, n + 2.0f);
-    }
-    const float m = v * t;
-    return 1.0f - __fdividef(2.0f, __expf(2.0f * m) + 1.0f);
-}
-
 // Weights of output channels [o0, o0 + 16*MB) x input channels [c0, c0 + CC), all 27 taps,
 // held in registers between the global load and the LDS store.
 // LDS layout (A-fragment order): ws[((tap*CC/4 + cg)*64 + lane)*MB + mb] holds
@@ -470,15 +454,21 @@ hipError_t launch_conv3d_mish_tanh(const float *x, const float *w, const float *
     return launch_act<1, 1, 2, 2, 4>(x, w, b, y, d, s);
 }
 
+hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
+                                hipStream_t s)
+{
+    hipLaunchKernelGGL(pool_sum_init_kernel, dim3((unsigned)cdiv(N, 256)), dim3(256), 0, s, bias,
+                       out, N, O);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *conv_b,
                                   const float *bias, float *out, const PoolDims &p,
                                   hipStream_t s)
 {
     constexpr int MB = 1, NBW = 4, WD = 1, WH = 4, CC = 4;
     const Conv3dDims &d = p.conv;
-    hipLaunchKernelGGL(pool_sum_init_kernel, dim3((unsigned)cdiv(d.N, 256)), dim3(256), 0, s,
-                       bias, out, d.N, d.O);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_pool_sum_init(bias, out, d.N, d.O, s);
     if (e != hipSuccess) return e;
     const int64_t tw = cdiv(p.PW, 8 * NBW), th = cdiv(p.PH, WH), td = cdiv(p.PD, WD);
     const int64_t og = cdiv(d.O, 16 * MB);

@@ -6,7 +6,9 @@
 
 namespace convfuse {
 
-// Shape of a cubic-kernel (k = 3), stride-1 Conv3d; O* are the output sizes.
+// Shape of a Conv3d with a cubic kernel; O* are the output sizes, pad the zero padding on
+// every side.  Kernel size and stride are implied (3 and 1) for the tuned kernels and given
+// by GenConv for the general ones.
 struct Conv3dDims {
     int64_t N, C, D, H, W, O;
     int64_t OD, OH, OW;
@@ -25,6 +27,12 @@ struct DwsepDims {
     int pad;
 };
 
+// Kernel size, stride and dilation of the general-parameter kernels.
+struct GenConv {
+    int k, stride, dilation;
+};
+
+// Tuned kernels: k = 3, stride 1, pad <= 2 (pool 2; dwsep dilation 1).
 hipError_t launch_conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
                                    const Conv3dDims &d, hipStream_t stream);
 
@@ -35,5 +43,24 @@ hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *c
 hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b,
                                const float *pw_w, const float *pw_b, float *y,
                                const DwsepDims &d, hipStream_t stream);
+
+// out[n] = sum_c bias[c] (the constant term of the pooled channel sum), on the stream.
+hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
+                                hipStream_t stream);
+
+// General-parameter kernels (any k, stride, padding, dilation; pooled sum: pool <= 32).
+hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const float *b,
+                                           float *y, const Conv3dDims &d, const GenConv &g,
+                                           hipStream_t stream);
+
+hipError_t launch_conv3d_pool_sum_generic(const float *x, const float *w, const float *conv_b,
+                                          const float *bias, float *out, const PoolDims &d,
+                                          const GenConv &g, int pool, hipStream_t stream);
+
+hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const float *dw_b,
+                                       const float *pw_w, const float *pw_b, float *y,
+                                       const DwsepDims &d, const GenConv &g, hipStream_t stream);
+
+constexpr int kGenericMaxPool = 32;  // largest pooling window of the general kernel
 
 }  // namespace convfuse

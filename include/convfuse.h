@@ -50,8 +50,9 @@ enum {
  *   w  [Cout][Cin][k][k][k]         device, read-only
  *   b  [Cout] or NULL (no bias)     device, read-only
  *   y  [N][Cout][OD][OH][OW]        device, written; OD = (D + 2*pad - k)/stride + 1, etc.
- * Supported on the GPU: k = 3, stride = 1, 0 <= pad <= 2; any N, Cin, Cout >= 1 and any
- * D, H, W that give a non-empty output.  Other k/stride return CONVFUSE_ERR_UNSUPPORTED.
+ * Any k, stride >= 1 and pad >= 0 that give a non-empty output, any N, Cin, Cout >= 1
+ * (page l2_p47's generalised stride/padding).  k = 3, stride = 1, pad <= 2 run the tuned
+ * kernel; other values a general kernel.  k^3 above 2^30 returns CONVFUSE_ERR_UNSUPPORTED.
  * Accumulation is fp32 on fp32 matrix cores; the epilogue runs in registers.
  */
 int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
@@ -76,7 +77,8 @@ int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
  * The whole reduction happens on the device; nothing is synchronised with the host.  The
  * channel/window partial sums meet through float atomics, so the last bits of out[n]
  * may differ from run to run.
- * Supported on the GPU: k = 3, pool = 2.  Other values return CONVFUSE_ERR_UNSUPPORTED.
+ * Any k; pool from 1 to 32 (k = 3, pool = 2 run the tuned kernel).  pool > 32 or k^3 above
+ * 2^30 return CONVFUSE_ERR_UNSUPPORTED.
  */
 int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
                                     float divisor, int64_t pool, const float *bias, float *out,
@@ -96,8 +98,9 @@ int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float 
  *   pw_b  [Cout] or NULL       device, read-only
  *   y     [N][Cout][Ho][Wo]    device, written; Ho = (H + 2p - d(K-1) - 1)/s + 1
  * The depthwise result stays on chip; only y is written.
- * Supported on the GPU: K = 3, stride = 1, dilation = 1, 0 <= pad <= 2.  Other values
- * return CONVFUSE_ERR_UNSUPPORTED.
+ * Any K, stride, pad, dilation that give a non-empty output (page l1_p86's generalised
+ * kernel).  K = 3, stride = 1, dilation = 1, pad <= 2 run the tuned kernels; other values a
+ * general kernel.  K^2 above 2^30 returns CONVFUSE_ERR_UNSUPPORTED.
  */
 int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                  const float *pw_b, float *y, int64_t N, int64_t Cin, int64_t H, int64_t W,

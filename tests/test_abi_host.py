@@ -1,6 +1,7 @@
 """Host-only checks of libconvfuse.so: it loads, exports every function include/convfuse.h
 declares, and rejects bad arguments with the documented codes before launching anything.
-No GPU is needed: every call here fails validation (or is an N = 0 no-op)."""
+No GPU is needed: every call here fails validation (or is an N = 0 no-op), so no kernel is
+launched with the fake pointers used below."""
 import ctypes
 import os
 import re
@@ -74,8 +75,8 @@ def call_dw(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W
     (dict(D=2), cf.ERR_SHAPE), (dict(W=0), cf.ERR_SHAPE), (dict(p=-1), cf.ERR_SHAPE),
     (dict(s=0), cf.ERR_SHAPE), (dict(C=1 << 40), cf.ERR_SHAPE),
     (dict(N=1 << 20, C=1 << 20, D=1 << 20, H=1 << 20), cf.ERR_SHAPE),
-    (dict(k=5), cf.ERR_UNSUPPORTED), (dict(s=2), cf.ERR_UNSUPPORTED),
-    (dict(p=3), cf.ERR_UNSUPPORTED), (dict(k=1), cf.ERR_UNSUPPORTED),
+    (dict(s=1 << 25), cf.ERR_SHAPE), (dict(D=1 << 25), cf.ERR_SHAPE),
+    (dict(k=1100, D=1 << 12, H=1 << 12, W=1 << 12, C=1, O=1), cf.ERR_UNSUPPORTED),
 ])
 def test_conv3d_mish_tanh_validation(kw, code):
     assert call_act(**kw) == code
@@ -87,7 +88,8 @@ def test_conv3d_mish_tanh_validation(kw, code):
     (dict(div=0.0), cf.ERR_SHAPE), (dict(div=float("inf")), cf.ERR_SHAPE),
     (dict(div=float("nan")), cf.ERR_SHAPE), (dict(D=3), cf.ERR_SHAPE),
     (dict(pool=0), cf.ERR_SHAPE), (dict(pool=9), cf.ERR_SHAPE), (dict(C=0), cf.ERR_SHAPE),
-    (dict(pool=3), cf.ERR_UNSUPPORTED), (dict(k=5), cf.ERR_UNSUPPORTED),
+    (dict(pool=33, D=66, H=66, W=66), cf.ERR_UNSUPPORTED),
+    (dict(k=1100, D=1 << 12, H=1 << 12, W=1 << 12, C=1, O=1), cf.ERR_UNSUPPORTED),
 ])
 def test_pool_validation(kw, code):
     assert call_pool(**kw) == code
@@ -98,8 +100,8 @@ def test_pool_validation(kw, code):
     (dict(x=None), cf.ERR_NULL), (dict(dw=None), cf.ERR_NULL), (dict(pw=None), cf.ERR_NULL),
     (dict(y=None), cf.ERR_NULL), (dict(C=0), cf.ERR_SHAPE), (dict(H=0), cf.ERR_SHAPE),
     (dict(p=0, H=2), cf.ERR_SHAPE), (dict(d=0), cf.ERR_SHAPE),
-    (dict(K=5, p=2), cf.ERR_UNSUPPORTED), (dict(s=2), cf.ERR_UNSUPPORTED),
-    (dict(d=2, p=2), cf.ERR_UNSUPPORTED), (dict(p=3), cf.ERR_UNSUPPORTED),
+    (dict(s=1 << 25), cf.ERR_SHAPE), (dict(K=1 << 25), cf.ERR_SHAPE),
+    (dict(K=40000, p=20000, C=1, O=1), cf.ERR_UNSUPPORTED),
 ])
 def test_dwsep_validation(kw, code):
     assert call_dw(**kw) == code
@@ -115,7 +117,7 @@ def test_empty_batch_is_a_no_op():
 
 def test_error_message_is_thread_local():
     import threading
-    assert call_act(k=5) == cf.ERR_UNSUPPORTED
+    assert call_act(C=0) == cf.ERR_SHAPE
     seen = {}
 
     def other():
