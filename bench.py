@@ -32,27 +32,42 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 BENCH_WORKLOADS = (2, 3, 4, 5)
 
 
+def _olen(n, k, s=1, p=0, d=1):
+    return (n + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def out_dims(w):
+    """Output spatial sizes of the convolution(s) of a workload."""
+    d, p = w.dims, w.params
+    if w.op == "dwsep_conv2d":
+        args = (p["K"], p["stride"], p["pad"], p["dilation"])
+        return _olen(d["H"], *args), _olen(d["W"], *args)
+    s, pad = p.get("stride", 1), p.get("pad", 0)
+    return tuple(_olen(d[a], p["k"], s, pad) for a in ("D", "H", "W"))
+
+
 def work(w):
     """Algorithmic multiply-adds and bytes (inputs + weights + outputs, each once)."""
     d, p = w.dims, w.params
     if w.op == "conv3d_mish_tanh":
         k = p["k"]
-        od, oh, ow = (d[s] - k + 1 for s in ("D", "H", "W"))
+        od, oh, ow = out_dims(w)
         outs = d["N"] * d["O"] * od * oh * ow
         macs = outs * d["C"] * k ** 3
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
                       + d["O"] + outs)
     elif w.op == "conv3d_div_maxpool_gap_bias_sum":
         k = p["k"]
-        od, oh, ow = (d[s] - k + 1 for s in ("D", "H", "W"))
+        od, oh, ow = out_dims(w)
         macs = d["N"] * d["O"] * od * oh * ow * d["C"] * k ** 3
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
                       + 2 * d["O"] + d["N"])
     else:
         K = p["K"]
-        pix = d["N"] * d["H"] * d["W"]   # stride 1, "same" padding: Ho = H, Wo = W
-        macs = pix * d["C"] * K * K + pix * d["O"] * d["C"]
-        nbytes = 4 * (pix * d["C"] + d["C"] * K * K + d["O"] * d["C"] + pix * d["O"]
+        ho, wo = out_dims(w)
+        pix_in, pix_out = d["N"] * d["H"] * d["W"], d["N"] * ho * wo
+        macs = pix_out * d["C"] * K * K + pix_out * d["O"] * d["C"]
+        nbytes = 4 * (pix_in * d["C"] + d["C"] * K * K + d["O"] * d["C"] + pix_out * d["O"]
                       + (d["C"] + d["O"] if p["bias"] else 0))
     return macs, nbytes
 
@@ -140,13 +155,12 @@ def run_op(cf, w, t, out):
 
 
 def out_shape(w):
-    d, p = w.dims, w.params
+    d = w.dims
     if w.op == "conv3d_mish_tanh":
-        k = p["k"]
-        return (d["N"], d["O"], d["D"] - k + 1, d["H"] - k + 1, d["W"] - k + 1)
+        return (d["N"], d["O"]) + out_dims(w)
     if w.op == "conv3d_div_maxpool_gap_bias_sum":
         return (d["N"],)
-    return (d["N"], d["O"], d["H"], d["W"])
+    return (d["N"], d["O"]) + out_dims(w)
 
 
 def cpu_baseline(workloads, frac_batch):

@@ -111,4 +111,13 @@ WORKLOADS = {
     5: Workload(5, "dwsep_conv2d_333x517_bias", "dwsep_conv2d",
                 dict(N=8, C=96, H=333, W=517, O=192),
                 dict(K=3, stride=1, pad=1, dilation=1, bias=True)),
+    # General-parameter variants of the same layers (kernel size, stride, pooling window),
+    # timed on request; they run the general kernels.
+    6: Workload(6, "conv3d_mish_tanh_k5_s2_p2", "conv3d_mish_tanh",
+                dict(N=16, C=32, D=32, H=64, W=64, O=64), dict(k=5, stride=2, pad=2)),
+    7: Workload(7, "conv3d_div_maxpool3_gap_bias_sum", "conv3d_div_maxpool_gap_bias_sum",
+                dict(N=128, C=8, D=16, H=64, W=64, O=16), dict(k=3, divisor=2.0, pool=3)),
+    8: Workload(8, "dwsep_conv2d_512_k5_s2", "dwsep_conv2d",
+                dict(N=16, C=64, H=512, W=512, O=128),
+                dict(K=5, stride=2, pad=2, dilation=1, bias=False)),
 }

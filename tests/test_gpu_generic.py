@@ -101,3 +101,38 @@ def test_dwsep_general_larger_sampled():
     ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"], idx,
                                  2, 4, 2)
     assert_close(gather(y, idx), ref, "dwsep K5 s2 d2 sampled")
+
+
+@pytest.mark.parametrize("index", [6, 8])
+def test_general_workload_sampled(index):
+    """The general-parameter workloads at the size bench.py times them: sampled outputs."""
+    w = wl.WORKLOADS[index]
+    inp = w.inputs()
+    p = w.params
+    rng = np.random.default_rng(20 + index)
+    if w.op == "conv3d_mish_tanh":
+        y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), p["stride"],
+                                  p["pad"])
+        idx = edge_indices(y.shape, rng, 8000)
+        ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
+    else:
+        y = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
+                              dev(inp["pw_b"]), p["stride"], p["pad"], p["dilation"])
+        idx = edge_indices(y.shape, rng, 8000)
+        ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"],
+                                     inp["pw_b"], idx, p["stride"], p["pad"], p["dilation"])
+    assert_close(gather(y, idx), ref, "workload %d sampled" % index)
+
+
+def test_general_pool_workload_picks():
+    w = wl.WORKLOADS[7]
+    inp = w.inputs()
+    p = w.params
+    out = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
+                                               p["divisor"], p["pool"], dev(inp["bias"]))
+    got = out.cpu().numpy().astype(np.float64)
+    picks = [0, 77, 127]
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"][picks], inp["w"], inp["conv_b"],
+                                                 p["divisor"], p["pool"], inp["bias"])
+    rel = np.abs(got[picks] - ref) / np.abs(ref)
+    assert rel.max() <= POOL_RTOL, (got[picks], ref)
