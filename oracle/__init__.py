@@ -55,6 +55,8 @@ def _load():
             [_f32p, _f32p, _f32p, _i64p, _i64, _f64p] + [_i64] * 9)
         lib.oracle_conv3d_div_maxpool_gap_bias_sum.argtypes = (
             [_f32p, _f32p, _f32p, ctypes.c_double, _i64, _f32p, _f64p] + [_i64] * 7)
+        lib.oracle_conv3d_div_maxpool.argtypes = (
+            [_f32p, _f32p, _f32p, ctypes.c_double, _i64, _f64p] + [_i64] * 7)
         lib.oracle_dwsep_conv2d.argtypes = (
             [_f32p, _f32p, _f32p, _f32p, _f32p, _f64p, _f64p] + [_i64] * 9)
         lib.oracle_dwsep_conv2d_at.argtypes = (
@@ -155,6 +157,23 @@ def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias):
         xp, wp, cbp, float(divisor), pool, biasp, out.ctypes.data_as(_f64p),
         N, C, D, H, W, O, k), "conv3d_div_maxpool_gap_bias_sum")
     return out
+
+
+def conv3d_div_maxpool(x, w, conv_b, divisor, pool):
+    """y = maxpool_pool((conv(x)+cb)/divisor), the pooled tensor [N,O,PD,PH,PW] (page l2_p8,
+    the fused conv + divide + max-pool output)."""
+    lib = _load()
+    x, xp = _f32(x)
+    w, wp = _f32(w)
+    conv_b, cbp = _f32(conv_b)
+    N, C, D, H, W = x.shape
+    O, _, k, _, _ = w.shape
+    dims = [out_len(out_len(s, k, 1, 0, 1), pool, pool, 0, 1) for s in (D, H, W)]
+    y = np.empty((N, O, *dims), np.float64)
+    _check(lib.oracle_conv3d_div_maxpool(xp, wp, cbp, float(divisor), pool,
+                                         y.ctypes.data_as(_f64p), N, C, D, H, W, O, k),
+           "conv3d_div_maxpool")
+    return y
 
 
 def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, pad=1, dilation=1):

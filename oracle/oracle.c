@@ -217,6 +217,46 @@ int oracle_conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const
     return 0;
 }
 
+/* y[n,o,pd,ph,pw] = max over the pool^3 window (stride pool, floor mode) of
+ * (conv3d(x)+cb)/divisor, valid conv (stride 1, no padding): the pooled tensor before the
+ * global mean (page l2_p8, the "Option A" output of the fused conv + divide + max-pool).
+ * y has N*O*PD*PH*PW entries. */
+int oracle_conv3d_div_maxpool(const float *x, const float *w, const float *cb, double divisor,
+                              int64_t pool, double *y, int64_t N, int64_t C, int64_t D,
+                              int64_t H, int64_t W, int64_t O, int64_t k)
+{
+    if (!x || !w || !y || N < 0 || C <= 0 || O <= 0 || k <= 0 || pool <= 0) return -1;
+    if (divisor == 0.0) return -1;
+    int64_t OD = or_out_len(D, k, 1, 0, 1), OH = or_out_len(H, k, 1, 0, 1),
+            OW = or_out_len(W, k, 1, 0, 1);
+    if (OD <= 0 || OH <= 0 || OW <= 0) return -2;
+    int64_t PD = or_out_len(OD, pool, pool, 0, 1), PH = or_out_len(OH, pool, pool, 0, 1),
+            PW = or_out_len(OW, pool, pool, 0, 1);
+    if (PD <= 0 || PH <= 0 || PW <= 0) return -2;
+    int64_t total = N * O * PD * PH * PW;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t t = i;
+        int64_t pw = t % PW; t /= PW;
+        int64_t ph = t % PH; t /= PH;
+        int64_t pd = t % PD; t /= PD;
+        int64_t o = t % O, n = t / O;
+        double m = 0.0;
+        int first = 1;
+        for (int64_t a = 0; a < pool; ++a)
+            for (int64_t bb = 0; bb < pool; ++bb)
+                for (int64_t cc = 0; cc < pool; ++cc) {
+                    double v = or_conv3d_point(x, w, cb, C, D, H, W, k, 1, 0, n, o,
+                                               pd * pool + a, ph * pool + bb, pw * pool + cc);
+                    v = v / divisor;
+                    if (first || v > m) m = v;
+                    first = 0;
+                }
+        y[i] = m;
+    }
+    return 0;
+}
+
 /* One depthwise output: bd[c] + sum_{kh,kw} wd[c,0,kh,kw] * x[n,c,h*s-p+kh*d, w*s-p+kw*d]. */
 static double or_depthwise_point(const float *x, const float *wd, const float *bd,
                                  int64_t C, int64_t H, int64_t W, int64_t K, int64_t s,

@@ -242,6 +242,56 @@ def test_pool_ramp_delta_floor_mode():
     np.testing.assert_allclose(got, 2 * (-(PW - 1)) / 2.0, rtol=1e-15)
 
 
+def np_conv_div_maxpool(x, w, cb, divisor, pool):
+    """Independent pooled tensor: numpy conv, + cb, / divisor, windows reshaped, max."""
+    co = np_conv3d(x, w, cb) / divisor
+    N, O, OD, OH, OW = co.shape
+    PD, PH, PW = (OD - pool) // pool + 1, (OH - pool) // pool + 1, (OW - pool) // pool + 1
+    c = co[:, :, :PD * pool, :PH * pool, :PW * pool]
+    return c.reshape(N, O, PD, pool, PH, pool, PW, pool).max(axis=(3, 5, 7))
+
+
+@pytest.mark.parametrize("shape,k,pool,div", [((2, 3, 8, 10, 12), 3, 2, 2.0),
+                                              ((1, 2, 9, 7, 11), 3, 2, -2.0),
+                                              ((2, 2, 11, 10, 13), 3, 3, 0.5),
+                                              ((1, 3, 7, 8, 9), 1, 4, 3.0),
+                                              ((1, 2, 10, 9, 12), 5, 2, 2.0)])
+def test_pooled_tensor_matches_numpy(shape, k, pool, div):
+    N, C, D, H, W = shape
+    x = rng.standard_normal(shape).astype(np.float32)
+    w = rng.uniform(-0.3, 0.3, (5, C, k, k, k)).astype(np.float32)
+    cb = rng.uniform(-0.3, 0.3, 5).astype(np.float32)
+    got = oracle.conv3d_div_maxpool(x, w, cb, div, pool)
+    ref = np_conv_div_maxpool(x, w, cb, div, pool)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_pooled_tensor_ramp_closed_form():
+    """Delta kernel on a ramp along W: window maxima are the odd columns (2pw+1), halved;
+    floor mode keeps (W-2)//2 windows of the 11-wide conv output."""
+    N, C, D, H, W = 1, 1, 6, 6, 13
+    ramp = np.broadcast_to(np.arange(W, dtype=np.float32), (N, C, D, H, W)).copy()
+    w = np.zeros((2, 1, 3, 3, 3), np.float32)
+    w[:, 0, 0, 0, 0] = 1.0
+    got = oracle.conv3d_div_maxpool(ramp, w, None, 2.0, 2)
+    PW = (W - 2) // 2
+    assert got.shape == (1, 2, 2, 2, PW)
+    np.testing.assert_array_equal(got, np.broadcast_to((2 * np.arange(PW) + 1) / 2.0, got.shape))
+
+
+def test_pooled_tensor_reduces_to_pooled_sum():
+    """Channel sum of (mean of the pooled tensor + bias) is the fused pooled-sum output."""
+    x = rng.standard_normal((3, 2, 7, 9, 10)).astype(np.float32)
+    w = rng.uniform(-0.3, 0.3, (4, 2, 3, 3, 3)).astype(np.float32)
+    cb = rng.uniform(-0.3, 0.3, 4).astype(np.float32)
+    bias = rng.standard_normal(4).astype(np.float32)
+    mp = oracle.conv3d_div_maxpool(x, w, cb, 2.0, 2)
+    via = (mp.mean(axis=(2, 3, 4)) + bias.astype(np.float64)[None]).sum(axis=1)
+    np.testing.assert_allclose(oracle.conv3d_div_maxpool_gap_bias_sum(x, w, cb, 2.0, 2, bias),
+                               via, rtol=1e-13)
+
+
 # ---------------------------------------------------------------- (c) depthwise-separable
 @pytest.mark.parametrize("K,stride,pad,dil,bias", [(3, 1, 1, 1, False), (3, 1, 1, 1, True),
                                                    (3, 2, 1, 1, True), (5, 1, 2, 2, False),
