@@ -56,12 +56,16 @@ def work(w):
         macs = outs * d["C"] * k ** 3
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
                       + d["O"] + outs)
-    elif w.op == "conv3d_div_maxpool_gap_bias_sum":
+    elif w.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
         k = p["k"]
         od, oh, ow = out_dims(w)
         macs = d["N"] * d["O"] * od * oh * ow * d["C"] * k ** 3
-        nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
-                      + 2 * d["O"] + d["N"])
+        nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3)
+        if w.op == "conv3d_div_maxpool":
+            pooled = [(s - p["pool"]) // p["pool"] + 1 for s in (od, oh, ow)]
+            nbytes += 4 * (d["O"] + d["N"] * d["O"] * pooled[0] * pooled[1] * pooled[2])
+        else:
+            nbytes += 4 * (2 * d["O"] + d["N"])
     else:
         K = p["K"]
         ho, wo = out_dims(w)
@@ -149,6 +153,8 @@ def run_op(cf, w, t, out):
     elif w.op == "conv3d_div_maxpool_gap_bias_sum":
         cf.conv3d_div_maxpool_gap_bias_sum(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"],
                                            t["bias"], out=out)
+    elif w.op == "conv3d_div_maxpool":
+        cf.conv3d_div_maxpool(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"], out=out)
     else:
         cf.dwsep_conv2d(t["x"], t["dw_w"], t["dw_b"], t["pw_w"], t["pw_b"], p["stride"],
                         p["pad"], p["dilation"], out=out)
@@ -160,6 +166,9 @@ def out_shape(w):
         return (d["N"], d["O"]) + out_dims(w)
     if w.op == "conv3d_div_maxpool_gap_bias_sum":
         return (d["N"],)
+    if w.op == "conv3d_div_maxpool":
+        pool = w.params["pool"]
+        return (d["N"], d["O"]) + tuple((s - pool) // pool + 1 for s in out_dims(w))
     return (d["N"], d["O"]) + out_dims(w)
 
 
@@ -180,6 +189,8 @@ def cpu_baseline(workloads, frac_batch):
         elif w.op == "conv3d_div_maxpool_gap_bias_sum":
             oracle.conv3d_div_maxpool_gap_bias_sum(x, inp["w"], inp["conv_b"], p["divisor"],
                                                    p["pool"], inp["bias"])
+        elif w.op == "conv3d_div_maxpool":
+            oracle.conv3d_div_maxpool(x, inp["w"], inp["conv_b"], p["divisor"], p["pool"])
         else:
             oracle.dwsep_conv2d(x, inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
                                 p["stride"], p["pad"], p["dilation"])
@@ -292,6 +303,7 @@ def main():
     dmacs, dbytes = work(dominant)
     kname = {"conv3d_mish_tanh": "conv3d_mish_tanh_kernel",
              "conv3d_div_maxpool_gap_bias_sum": "conv3d_pool_sum_kernel",
+             "conv3d_div_maxpool": "conv3d_pool_sum_kernel",
              "dwsep_conv2d": "dwsep_persistent_kernel"}[dominant.op]
     achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,

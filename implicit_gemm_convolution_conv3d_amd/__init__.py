@@ -15,7 +15,8 @@ import threading
 from . import _build
 
 __all__ = [
-    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d", "conv_out_len",
+    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
+    "conv_out_len",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -24,7 +25,7 @@ _ERR_NAMES = {ERR_NULL: "NULL", ERR_SHAPE: "SHAPE", ERR_UNSUPPORTED: "UNSUPPORTE
               ERR_DEVICE: "DEVICE"}
 
 EXPORTED_SYMBOLS = (
-    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d",
+    "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
 )
 
@@ -55,6 +56,8 @@ def lib():
             L.conv3d_mish_tanh.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.conv3d_div_maxpool_gap_bias_sum.argtypes = (
                 [_vp] * 3 + [ctypes.c_float, _i64, _vp, _vp] + [_i64] * 7 + [_vp])
+            L.conv3d_div_maxpool.argtypes = (
+                [_vp] * 3 + [ctypes.c_float, _i64, _vp] + [_i64] * 7 + [_vp])
             L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
             L.convfuse_conv_out_len.argtypes = [_i64] * 5 + [ctypes.POINTER(_i64)]
             L.convfuse_last_error.restype = ctypes.c_char_p
@@ -135,6 +138,25 @@ def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out=None)
         _check(lib().conv3d_div_maxpool_gap_bias_sum(
             _ptr(x, "x"), _ptr(w, "w"), _ptr(conv_b, "conv_b"), float(divisor), pool,
             _ptr(bias, "bias"), _ptr(out, "out", (N,)), N, C, D, H, W, O, k, _stream(x)))
+    return out
+
+
+def conv3d_div_maxpool(x, w, conv_b, divisor, pool, out=None):
+    """y = maxpool_pool((conv3d(x,w)+conv_b)/divisor); y [N, Cout, PD, PH, PW]."""
+    import torch
+    N, C, D, H, W = x.shape
+    O, C2, k = w.shape[0], w.shape[1], w.shape[2]
+    if C2 != C or tuple(w.shape[2:]) != (k, k, k):
+        raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
+    if conv_b is not None and tuple(conv_b.shape) != (O,):
+        raise ValueError("conv_b must have shape (%d,)" % O)
+    shp = (N, O) + tuple(conv_out_len(conv_out_len(s, k), pool, pool) for s in (D, H, W))
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().conv3d_div_maxpool(
+            _ptr(x, "x"), _ptr(w, "w"), _ptr(conv_b, "conv_b"), float(divisor), pool,
+            _ptr(out, "out", shp), N, C, D, H, W, O, k, _stream(x)))
     return out
 
 

@@ -169,6 +169,48 @@ int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float 
                          "conv3d_div_maxpool_gap_bias_sum launch");
 }
 
+int conv3d_div_maxpool(const float *x, const float *w, const float *conv_b, float divisor,
+                       int64_t pool, float *y, int64_t N, int64_t Cin, int64_t D, int64_t H,
+                       int64_t W, int64_t Cout, int64_t k, void *stream)
+{
+    const char *fn = "conv3d_div_maxpool";
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
+                    (long long)Cin, (long long)Cout);
+    if (!std::isfinite(divisor) || divisor == 0.0f)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: divisor must be finite and non-zero", fn);
+    int64_t OD, OH, OW, PD, PH, PW;
+    if (!out_len(D, k, 1, 0, 1, &OD) || !out_len(H, k, 1, 0, 1, &OH) ||
+        !out_len(W, k, 1, 0, 1, &OW) || OD <= 0 || OH <= 0 || OW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: D=%lld H=%lld W=%lld k=%lld give no conv output", fn,
+                    (long long)D, (long long)H, (long long)W, (long long)k);
+    if (!out_len(OD, pool, pool, 0, 1, &PD) || !out_len(OH, pool, pool, 0, 1, &PH) ||
+        !out_len(OW, pool, pool, 0, 1, &PW) || PD <= 0 || PH <= 0 || PW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: pool=%lld does not fit the %lldx%lldx%lld conv output",
+                    fn, (long long)pool, (long long)OD, (long long)OH, (long long)OW);
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}) ||
+        !elems_ok({Cout, Cin, k, k, k}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (!taps_ok(k, 3))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: k=%lld: more than 2^30 taps", fn,
+                    (long long)k);
+    if (pool > convfuse::kGenericMaxPool)
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: GPU path implements pool<=%d (got pool=%lld)",
+                    fn, convfuse::kGenericMaxPool, (long long)pool);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "%s: x, w and y are required", fn);
+    convfuse::PoolDims p{{N, Cin, D, H, W, Cout, OD, OH, OW, 0}, PD, PH, PW, divisor};
+    if (k == 3 && pool == 2)
+        return device_status(
+            convfuse::launch_conv3d_div_maxpool(x, w, conv_b, y, p, (hipStream_t)stream),
+            "conv3d_div_maxpool launch");
+    const convfuse::GenConv g{(int)k, 1, 1};
+    return device_status(convfuse::launch_conv3d_div_maxpool_generic(x, w, conv_b, y, p, g,
+                                                                     (int)pool,
+                                                                     (hipStream_t)stream),
+                         "conv3d_div_maxpool launch");
+}
+
 int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                  const float *pw_b, float *y, int64_t N, int64_t Cin, int64_t H, int64_t W,
                  int64_t Cout, int64_t K, int64_t stride, int64_t pad, int64_t dilation,

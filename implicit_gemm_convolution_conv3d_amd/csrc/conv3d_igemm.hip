@@ -271,7 +271,10 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
 // voxel blocks are (dd, dh, q): conv voxel (2pd + dd, 2ph + dh, 2pw0 + 16q + j) for lane
 // column j, so the max over (dd, dh) is taken inside a lane and the max over the window's
 // two columns between lanes j and j^1.
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool PREFETCH>
+// STORE: instead of the sum, write each window's (max + cb) / divisor to the pooled tensor
+// y [N][O][PD][PH][PW] (the divided max: division by a constant is monotone, so this is the
+// max of the divided values, rounding included).
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool PREFETCH, bool STORE>
 __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     float *__restrict__ out, PoolDims pd_, int64_t tiles, int tiles_w, int tiles_h,
@@ -363,7 +366,13 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
                     const float m2 = __shfl_xor(m, 1, 64);
                     m = use_min ? fminf(m, m2) : fmaxf(m, m2);
                     const int pw = pw0 + 8 * q + (j >> 1);
-                    if (o < d.O && (j & 1) == 0 && pw < pd_.PW) part += (m + cbv) / pd_.divisor;
+                    if (o < d.O && (j & 1) == 0 && pw < pd_.PW) {
+                        const float v = (m + cbv) / pd_.divisor;
+                        if constexpr (STORE)
+                            out[(((n * d.O + o) * pd_.PD + pdi) * pd_.PH + phi) * pd_.PW + pw] = v;
+                        else
+                            part += v;
+                    }
                 }
             }
     } else {
@@ -374,6 +383,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
             next(c0);
         }
     }
+    if constexpr (STORE) return;  // (no barrier follows: every wave returns here)
     part = wave_sum(part);
     if (lane == 0) red[wave] = part;
     __syncthreads();
@@ -430,12 +440,12 @@ hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
     return hipGetLastError();
 }
 
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool STORE>
 void launch_pool_kernel(const float *x, const float *w, const float *conv_b, float *out,
                         const PoolDims &p, int64_t tiles, int64_t tw, int64_t th, int64_t td,
                         float inv_count, hipStream_t s)
 {
-    hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, VEC, BUF, BUF>),
+    hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, VEC, BUF, BUF, STORE>),
                        dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
                        tiles, (int)tw, (int)th, (int)td, inv_count);
 }
@@ -462,25 +472,42 @@ hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_
     return hipGetLastError();
 }
 
-hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *conv_b,
-                                  const float *bias, float *out, const PoolDims &p,
-                                  hipStream_t s)
+namespace {
+
+template <bool STORE>
+hipError_t launch_pool(const float *x, const float *w, const float *conv_b, float *out,
+                       const PoolDims &p, hipStream_t s)
 {
     constexpr int MB = 1, NBW = 4, WD = 1, WH = 4, CC = 4;
     const Conv3dDims &d = p.conv;
-    hipError_t e = launch_pool_sum_init(bias, out, d.N, d.O, s);
-    if (e != hipSuccess) return e;
     const int64_t tw = cdiv(p.PW, 8 * NBW), th = cdiv(p.PH, WH), td = cdiv(p.PD, WD);
     const int64_t og = cdiv(d.O, 16 * MB);
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
     const bool v = vec_ok(x, d.W), bf = buf_ok(d, CC);
-    if (v && bf) launch_pool_kernel<MB, NBW, WD, WH, CC, true, true>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
-    else if (v) launch_pool_kernel<MB, NBW, WD, WH, CC, true, false>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
-    else if (bf) launch_pool_kernel<MB, NBW, WD, WH, CC, false, true>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
-    else launch_pool_kernel<MB, NBW, WD, WH, CC, false, false>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    if (v && bf) launch_pool_kernel<MB, NBW, WD, WH, CC, true, true, STORE>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else if (v) launch_pool_kernel<MB, NBW, WD, WH, CC, true, false, STORE>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else if (bf) launch_pool_kernel<MB, NBW, WD, WH, CC, false, true, STORE>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
+    else launch_pool_kernel<MB, NBW, WD, WH, CC, false, false, STORE>(x, w, conv_b, out, p, tiles, tw, th, td, inv_count, s);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_pool_sum(const float *x, const float *w, const float *conv_b,
+                                  const float *bias, float *out, const PoolDims &p,
+                                  hipStream_t s)
+{
+    const hipError_t e = launch_pool_sum_init(bias, out, p.conv.N, p.conv.O, s);
+    if (e != hipSuccess) return e;
+    return launch_pool<false>(x, w, conv_b, out, p, s);
+}
+
+hipError_t launch_conv3d_div_maxpool(const float *x, const float *w, const float *conv_b,
+                                     float *y, const PoolDims &p, hipStream_t s)
+{
+    return launch_pool<true>(x, w, conv_b, y, p, s);
 }
 
 }  // namespace convfuse

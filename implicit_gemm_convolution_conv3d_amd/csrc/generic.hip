@@ -122,7 +122,8 @@ __global__ __launch_bounds__(64 * kGenWaves) void conv3d_mish_tanh_generic_kerne
 // of its P*TWP conv columns, divides (conv + cb) by the divisor (the definition's order)
 // and keeps the running maximum per (channel, column); the column maxima of each window are
 // then taken through LDS.  One atomicAdd per wave adds its windows' sum / count to out[n].
-template <int MB, int NB>
+// STORE: write each window's maximum to the pooled tensor out [N][O][PD][PH][PW] instead.
+template <int MB, int NB, bool STORE>
 __global__ __launch_bounds__(64 * kGenWaves) void conv3d_pool_sum_generic_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     float *__restrict__ out, PoolDims p, GenConv g, int pool, int64_t tiles, int tiles_w,
@@ -186,8 +187,12 @@ __global__ __launch_bounds__(64 * kGenWaves) void conv3d_pool_sum_generic_kernel
         if (o >= d.O || pw >= p.PW) continue;
         float v = mx[wave][ol][q * pool];
         for (int i = 1; i < pool; ++i) v = fmaxf(v, mx[wave][ol][q * pool + i]);
-        part += v;
+        if constexpr (STORE)
+            out[(((n * d.O + o) * p.PD + pd) * p.PH + ph) * p.PW + pw] = v;
+        else
+            part += v;
     }
+    if constexpr (STORE) return;
     part = wave_sum(part);
     if (lane == 0) atomicAdd(out + n, part * inv_count);
 }
@@ -294,25 +299,44 @@ hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const
     return hipGetLastError();
 }
 
-hipError_t launch_conv3d_pool_sum_generic(const float *x, const float *w, const float *conv_b,
-                                          const float *bias, float *out, const PoolDims &p,
-                                          const GenConv &g, int pool, hipStream_t s)
+namespace {
+
+template <bool STORE>
+hipError_t launch_pool_generic(const float *x, const float *w, const float *conv_b, float *out,
+                               const PoolDims &p, const GenConv &g, int pool, hipStream_t s)
 {
     constexpr int MB = 1, NB = 2;
     const Conv3dDims &d = p.conv;
     if (pool < 1 || pool > 16 * NB || pool > kGenericMaxPool) return hipErrorInvalidValue;
-    hipError_t e = launch_pool_sum_init(bias, out, d.N, d.O, s);
-    if (e != hipSuccess) return e;
     const int twp = 16 * NB / pool;
     const int64_t tw = cdiv(p.PW, twp);
     const int64_t tiles = cdiv(d.O, 16 * MB) * d.N * p.PD * p.PH * tw;
     unsigned grid;
-    if ((e = launch_waves(tiles, grid))) return e;
+    if (hipError_t e = launch_waves(tiles, grid)) return e;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
-    hipLaunchKernelGGL((conv3d_pool_sum_generic_kernel<MB, NB>), dim3(grid),
+    hipLaunchKernelGGL((conv3d_pool_sum_generic_kernel<MB, NB, STORE>), dim3(grid),
                        dim3(64 * kGenWaves), 0, s, x, w, conv_b, out, p, g, pool, tiles, (int)tw,
                        inv_count);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_pool_sum_generic(const float *x, const float *w, const float *conv_b,
+                                          const float *bias, float *out, const PoolDims &p,
+                                          const GenConv &g, int pool, hipStream_t s)
+{
+    if (pool < 1 || pool > kGenericMaxPool) return hipErrorInvalidValue;
+    const hipError_t e = launch_pool_sum_init(bias, out, p.conv.N, p.conv.O, s);
+    if (e != hipSuccess) return e;
+    return launch_pool_generic<false>(x, w, conv_b, out, p, g, pool, s);
+}
+
+hipError_t launch_conv3d_div_maxpool_generic(const float *x, const float *w,
+                                             const float *conv_b, float *y, const PoolDims &p,
+                                             const GenConv &g, int pool, hipStream_t s)
+{
+    return launch_pool_generic<true>(x, w, conv_b, y, p, g, pool, s);
 }
 
 hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const float *dw_b,

@@ -44,6 +44,10 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
                                const float *pw_w, const float *pw_b, float *y,
                                const DwsepDims &d, hipStream_t stream);
 
+// The pooled tensor y [N][O][PD][PH][PW] = maxpool((conv + conv_b) / divisor) (k = 3, pool 2).
+hipError_t launch_conv3d_div_maxpool(const float *x, const float *w, const float *conv_b,
+                                     float *y, const PoolDims &d, hipStream_t stream);
+
 // out[n] = sum_c bias[c] (the constant term of the pooled channel sum), on the stream.
 hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
                                 hipStream_t stream);
@@ -56,6 +60,10 @@ hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const
 hipError_t launch_conv3d_pool_sum_generic(const float *x, const float *w, const float *conv_b,
                                           const float *bias, float *out, const PoolDims &d,
                                           const GenConv &g, int pool, hipStream_t stream);
+
+hipError_t launch_conv3d_div_maxpool_generic(const float *x, const float *w,
+                                             const float *conv_b, float *y, const PoolDims &d,
+                                             const GenConv &g, int pool, hipStream_t stream);
 
 hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const float *dw_b,
                                        const float *pw_w, const float *pw_b, float *y,

@@ -89,7 +89,7 @@ class Workload:
         if self.op == "conv3d_mish_tanh":
             return conv3d_act_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                      self.params["k"], bias=True)
-        if self.op == "conv3d_div_maxpool_gap_bias_sum":
+        if self.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
             return conv3d_pool_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                       self.params["k"], conv_bias=True)
         if self.op == "dwsep_conv2d":
@@ -120,4 +120,7 @@ WORKLOADS = {
     8: Workload(8, "dwsep_conv2d_512_k5_s2", "dwsep_conv2d",
                 dict(N=16, C=64, H=512, W=512, O=128),
                 dict(K=5, stride=2, pad=2, dilation=1, bias=False)),
+    # The pooling layer with its pooled tensor [N,O,7,31,31] as the output (no global mean).
+    9: Workload(9, "conv3d_div_maxpool", "conv3d_div_maxpool",
+                dict(N=128, C=8, D=16, H=64, W=64, O=16), dict(k=3, divisor=2.0, pool=2)),
 }

@@ -86,6 +86,24 @@ int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float 
                                     int64_t Cout, int64_t k, void *stream);
 
 /*
+ * y = maxpool_pool( (conv3d(x, w) + conv_b) / divisor ): the pooled tensor of the fused
+ * conv + divide + max-pool, before the global mean (page "Kimi-K2.6 l2_p8", the option
+ * that writes the [N,C,7,31,31] pooled output for callers that need it).  Valid conv
+ * (stride 1, no padding), pool^3 windows of stride pool, floor mode.
+ *
+ *   x       [N][Cin][D][H][W]       device, read-only
+ *   w       [Cout][Cin][k][k][k]    device, read-only
+ *   conv_b  [Cout] or NULL          device, read-only
+ *   divisor finite and non-zero
+ *   y       [N][Cout][PD][PH][PW]   device, written; PD = (D - k + 1 - pool)/pool + 1, etc.
+ * The conv output never reaches memory.  Any k; pool from 1 to 32 (k = 3, pool = 2 run the
+ * tuned kernel); pool > 32 or k^3 above 2^30 return CONVFUSE_ERR_UNSUPPORTED.
+ */
+int conv3d_div_maxpool(const float *x, const float *w, const float *conv_b, float divisor,
+                       int64_t pool, float *y, int64_t N, int64_t Cin, int64_t D, int64_t H,
+                       int64_t W, int64_t Cout, int64_t k, void *stream);
+
+/*
  * y = pointwise(depthwise(x)):
  *   dw[n,c,h,w] = dw_b[c] + sum_{kh,kw} dw_w[c,0,kh,kw] * x[n,c,h*s-p+kh*d, w*s-p+kw*d]
  *   y[n,o,h,w]  = pw_b[o] + sum_c pw_w[o,c,0,0] * dw[n,c,h,w]

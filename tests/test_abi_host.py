@@ -96,6 +96,23 @@ def test_pool_validation(kw, code):
     assert "conv3d_div_maxpool_gap_bias_sum" in cf.lib().convfuse_last_error().decode()
 
 
+def call_maxpool(x=FAKE, w=FAKE, cb=None, div=2.0, pool=2, y=FAKE, N=1, C=4, D=8, H=8, W=8,
+                 O=8, k=3):
+    return cf.lib().conv3d_div_maxpool(x, w, cb, div, pool, y, N, C, D, H, W, O, k, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(w=None), cf.ERR_NULL), (dict(y=None), cf.ERR_NULL),
+    (dict(div=0.0), cf.ERR_SHAPE), (dict(div=float("nan")), cf.ERR_SHAPE),
+    (dict(D=3), cf.ERR_SHAPE), (dict(pool=0), cf.ERR_SHAPE), (dict(pool=9), cf.ERR_SHAPE),
+    (dict(C=0), cf.ERR_SHAPE), (dict(O=-1), cf.ERR_SHAPE),
+    (dict(pool=33, D=66, H=66, W=66), cf.ERR_UNSUPPORTED),
+])
+def test_maxpool_validation(kw, code):
+    assert call_maxpool(**kw) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("conv3d_div_maxpool")
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), cf.ERR_NULL), (dict(dw=None), cf.ERR_NULL), (dict(pw=None), cf.ERR_NULL),
     (dict(y=None), cf.ERR_NULL), (dict(C=0), cf.ERR_SHAPE), (dict(H=0), cf.ERR_SHAPE),
@@ -112,6 +129,7 @@ def test_empty_batch_is_a_no_op():
     # N = 0: nothing to compute, no pointer is needed and nothing is launched.
     assert call_act(x=None, w=None, y=None, N=0) == cf.OK
     assert call_pool(x=None, w=None, bias=None, out=None, N=0) == cf.OK
+    assert call_maxpool(x=None, w=None, y=None, N=0) == cf.OK
     assert call_dw(x=None, dw=None, pw=None, y=None, N=0) == cf.OK
 
 

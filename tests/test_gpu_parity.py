@@ -169,6 +169,41 @@ def test_pool_full_workload_sampled():
     assert np.max(np.abs(got2 - got) / np.abs(got)) <= 1e-5
 
 
+# ----------------------------------------------------------------- conv3d + pool (tensor)
+MAXPOOL_CASES = [
+    # (N, C, D, H, W, O, k, pool, divisor, conv_bias)
+    (3, 8, 6, 10, 12, 16, 3, 2, 2.0, True),     # tuned kernel
+    (2, 5, 9, 11, 70, 21, 3, 2, 2.0, True),     # floor mode, two channel groups, ragged W
+    (2, 4, 4, 20, 36, 16, 3, 2, -2.0, True),    # negative divisor
+    (1, 3, 5, 5, 5, 7, 3, 2, 3.0, False),       # single window
+    (2, 4, 8, 9, 21, 16, 3, 3, 2.0, True),      # general kernel: pool 3
+    (1, 3, 9, 9, 40, 7, 5, 2, -1.5, True),      # general kernel: k = 5
+]
+
+
+@pytest.mark.parametrize("case", MAXPOOL_CASES)
+def test_maxpool_tensor_small(case):
+    N, C, D, H, W, O, k, pool, div, cbias = case
+    inp = wl.conv3d_pool_inputs(700 + int(sum(case)), N, C, D, H, W, O, k=k, conv_bias=cbias)
+    ref = oracle.conv3d_div_maxpool(inp["x"], inp["w"], inp["conv_b"], div, pool)
+    y = cf().conv3d_div_maxpool(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]), div, pool)
+    assert tuple(y.shape) == ref.shape
+    assert_close(y.cpu().numpy(), ref, "conv3d_div_maxpool %s" % (case,))
+
+
+def test_maxpool_tensor_workload_shape():
+    """The pooling workload's shape, pooled tensor [128,16,7,31,31]: batch items 0 and 127
+    in full against the oracle, every element finite."""
+    w2 = wl.WORKLOADS[2]
+    inp = w2.inputs()
+    y = cf().conv3d_div_maxpool(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]), 2.0, 2)
+    assert tuple(y.shape) == (128, 16, 7, 31, 31)
+    picks = [0, 127]
+    ref = oracle.conv3d_div_maxpool(inp["x"][picks], inp["w"], inp["conv_b"], 2.0, 2)
+    assert_close(y[picks].cpu().numpy(), ref, "pooled tensor, workload shape")
+    assert bool(_torch().isfinite(y).all())
+
+
 # ----------------------------------------------------------------- depthwise-separable
 DW_CASES = [
     # (N, C, H, W, O, pad, bias)
