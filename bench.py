@@ -202,6 +202,70 @@ def cpu_baseline(workloads, frac_batch):
     return 2 * total_macs / secs / 1e12, oracle.threads(), desc
 
 
+def ablation(cf, wls, steps, warmup):
+    """Fused entry point against the unfused path built from the same kernels (conv writing
+    its output, then the epilogue or reduction as separate kernels; depthwise writing its
+    intermediate, then pointwise), per workload, timed with HIP events on the stream."""
+    import torch
+    res = {}
+    for w in wls:
+        inp = w.inputs()
+        t = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inp.items()}
+        del inp
+        p, d = w.params, w.dims
+        fused_out = torch.empty(out_shape(w), device="cuda")
+        if w.op == "conv3d_mish_tanh":
+            inter = torch.empty(out_shape(w), device="cuda")
+
+            def unfused():
+                cf.conv3d_bias(t["x"], t["w"], t["b"], p["stride"], p["pad"], out=inter)
+                cf.mish_tanh(inter, out=inter)
+        elif w.op == "conv3d_div_maxpool_gap_bias_sum":
+            od, oh, ow = out_dims(w)
+            inter = torch.empty((d["N"], d["O"], od, oh, ow), device="cuda")
+
+            def unfused():
+                cf.conv3d_bias(t["x"], t["w"], t["conv_b"], out=inter)
+                cf.div_maxpool_gap_bias_sum(inter, p["divisor"], p["pool"], t["bias"],
+                                            out=fused_out)
+        elif w.op == "dwsep_conv2d":
+            ho, wo = out_dims(w)
+            inter = torch.empty((d["N"], d["C"], ho, wo), device="cuda")
+            if (p["stride"], p["dilation"]) != (1, 1):
+                continue
+
+            def unfused():
+                cf.depthwise_conv2d(t["x"], t["dw_w"], t["dw_b"], p["stride"], p["pad"],
+                                    p["dilation"], out=inter)
+                cf.pointwise_conv2d(inter, t["pw_w"], t["pw_b"], out=fused_out)
+        else:
+            continue
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+        ms_f = timed(lambda: run_op(cf, w, t, fused_out))
+        ms_u = timed(unfused)
+        macs, nbytes = work(w)
+        res[w.name] = {"fused_ms": round(ms_f, 4), "unfused_ms": round(ms_u, 4),
+                       "speedup": round(ms_u / ms_f, 3),
+                       "intermediate_mb": round(inter.numel() * 4 / 1e6, 1),
+                       "fused_tflops": round(2 * macs / ms_f / 1e9, 2)}
+        del t, fused_out, inter
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +284,9 @@ def main():
                          "WRITE_SIZE) of runs that included --copy-calibration-mib into "
                          "profiles/traffic.json")
     ap.add_argument("--calibration-mib", type=int, default=1024)
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the benchmark, time each workload fused and unfused "
+                         "(separate conv/epilogue/reduce or depthwise/pointwise kernels)")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.calibration_mib)
@@ -251,6 +318,10 @@ def main():
     dev = torch.device("cuda:0")
     ids = [int(s) for s in args.workloads.split(",") if s]
     wls = [wl.WORKLOADS[i] for i in ids]
+    if args.ablation:
+        print(json.dumps({"ablation": ablation(cf, wls, args.steps, args.warmup),
+                          "kernel_source_sha": kernel_source_sha()}), flush=True)
+        return
 
     tensors, outs = [], []
     for w in wls:

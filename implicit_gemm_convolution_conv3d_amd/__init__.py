@@ -16,7 +16,8 @@ from . import _build
 
 __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
-    "conv_out_len",
+    "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
+    "pointwise_conv2d", "conv_out_len",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -26,6 +27,8 @@ _ERR_NAMES = {ERR_NULL: "NULL", ERR_SHAPE: "SHAPE", ERR_UNSUPPORTED: "UNSUPPORTE
 
 EXPORTED_SYMBOLS = (
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
+    "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
+    "pointwise_conv2d",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
 )
 
@@ -59,6 +62,12 @@ def lib():
             L.conv3d_div_maxpool.argtypes = (
                 [_vp] * 3 + [ctypes.c_float, _i64, _vp] + [_i64] * 7 + [_vp])
             L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
+            L.conv3d_bias.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
+            L.mish_tanh.argtypes = [_vp, _vp, _i64, _vp]
+            L.div_maxpool_gap_bias_sum.argtypes = (
+                [_vp, ctypes.c_float, _i64, _vp, _vp] + [_i64] * 5 + [_vp])
+            L.depthwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 8 + [_vp]
+            L.pointwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 5 + [_vp]
             L.convfuse_conv_out_len.argtypes = [_i64] * 5 + [ctypes.POINTER(_i64)]
             L.convfuse_last_error.restype = ctypes.c_char_p
             L.convfuse_abi_version.restype = ctypes.c_int
@@ -181,4 +190,83 @@ def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out
         _check(lib().dwsep_conv2d(_ptr(x, "x"), _ptr(dw_w, "dw_w"), _ptr(dw_b, "dw_b"),
                                   _ptr(pw_w, "pw_w"), _ptr(pw_b, "pw_b"), _ptr(out, "out", shp),
                                   N, C, H, W, O, K, stride, padding, dilation, _stream(x)))
+    return out
+
+
+# ----------------------------------------------------------------- unfused path steps
+def conv3d_bias(x, w, b=None, stride=1, padding=0, out=None):
+    """y = conv3d(x, w) + b (the unfused path's convolution); y [N, Cout, OD, OH, OW]."""
+    import torch
+    N, C, D, H, W = x.shape
+    O, C2, k = w.shape[0], w.shape[1], w.shape[2]
+    if C2 != C or tuple(w.shape[2:]) != (k, k, k):
+        raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
+    if b is not None and tuple(b.shape) != (O,):
+        raise ValueError("bias must have shape (%d,)" % O)
+    shp = (N, O) + tuple(conv_out_len(s, k, stride, padding) for s in (D, H, W))
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().conv3d_bias(_ptr(x, "x"), _ptr(w, "w"), _ptr(b, "b"), _ptr(out, "out", shp),
+                                 N, C, D, H, W, O, k, stride, padding, _stream(x)))
+    return out
+
+
+def mish_tanh(v, out=None):
+    """y = tanh(mish(v)) elementwise (out may be v)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(v)
+    with torch.cuda.device(v.device):
+        _check(lib().mish_tanh(_ptr(v, "v"), _ptr(out, "out", tuple(v.shape)), v.numel(),
+                               _stream(v)))
+    return out
+
+
+def div_maxpool_gap_bias_sum(conv, divisor, pool, bias, out=None):
+    """out[n] = sum_c(mean(maxpool(conv/divisor)) + bias[c]) from a stored conv output."""
+    import torch
+    N, C, OD, OH, OW = conv.shape
+    if bias.numel() != C:
+        raise ValueError("bias must have %d elements" % C)
+    if out is None:
+        out = torch.empty((N,), dtype=torch.float32, device=conv.device)
+    with torch.cuda.device(conv.device):
+        _check(lib().div_maxpool_gap_bias_sum(_ptr(conv, "conv"), float(divisor), pool,
+                                              _ptr(bias, "bias"), _ptr(out, "out", (N,)),
+                                              N, C, OD, OH, OW, _stream(conv)))
+    return out
+
+
+def depthwise_conv2d(x, dw_w, dw_b=None, stride=1, padding=1, dilation=1, out=None):
+    """y = depthwise conv of x (+ dw_b); y [N, C, Ho, Wo]."""
+    import torch
+    N, C, H, W = x.shape
+    K = dw_w.shape[-1]
+    if tuple(dw_w.shape) != (C, 1, K, K):
+        raise ValueError("dw_w %s does not match input %s" % (tuple(dw_w.shape), tuple(x.shape)))
+    shp = (N, C, conv_out_len(H, K, stride, padding, dilation),
+           conv_out_len(W, K, stride, padding, dilation))
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().depthwise_conv2d(_ptr(x, "x"), _ptr(dw_w, "dw_w"), _ptr(dw_b, "dw_b"),
+                                      _ptr(out, "out", shp), N, C, H, W, K, stride, padding,
+                                      dilation, _stream(x)))
+    return out
+
+
+def pointwise_conv2d(x, pw_w, pw_b=None, out=None):
+    """y = 1x1 conv of x (+ pw_b); x [N, Cin, H, W] -> y [N, Cout, H, W]."""
+    import torch
+    N, C, H, W = x.shape
+    O = pw_w.shape[0]
+    if tuple(pw_w.shape) != (O, C, 1, 1):
+        raise ValueError("pw_w %s does not match input %s" % (tuple(pw_w.shape), tuple(x.shape)))
+    shp = (N, O, H, W)
+    if out is None:
+        out = torch.empty(shp, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib().pointwise_conv2d(_ptr(x, "x"), _ptr(pw_w, "pw_w"), _ptr(pw_b, "pw_b"),
+                                      _ptr(out, "out", shp), N, C, H, W, O, _stream(x)))
     return out

@@ -246,4 +246,116 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                          "dwsep_conv2d launch");
 }
 
+// ------------------------------------------------------------------ unfused path steps
+
+int conv3d_bias(const float *x, const float *w, const float *b, float *y, int64_t N,
+                int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout, int64_t k,
+                int64_t stride, int64_t pad, void *stream)
+{
+    const char *fn = "conv3d_bias";
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
+                    (long long)Cin, (long long)Cout);
+    int64_t OD, OH, OW;
+    if (!out_len(D, k, stride, pad, 1, &OD) || !out_len(H, k, stride, pad, 1, &OH) ||
+        !out_len(W, k, stride, pad, 1, &OW) || OD <= 0 || OH <= 0 || OW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: D=%lld H=%lld W=%lld k=%lld stride=%lld pad=%lld "
+                    "give no output", fn, (long long)D, (long long)H, (long long)W, (long long)k,
+                    (long long)stride, (long long)pad);
+    if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}) ||
+        !elems_ok({Cout, Cin, k, k, k}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (!taps_ok(k, 3))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: k=%lld: more than 2^30 taps", fn, (long long)k);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "%s: x, w and y are required", fn);
+    convfuse::Conv3dDims d{N, Cin, D, H, W, Cout, OD, OH, OW, (int)pad};
+    if (k == 3 && stride == 1 && pad <= 2)
+        return device_status(convfuse::launch_conv3d_bias(x, w, b, y, d, (hipStream_t)stream),
+                             "conv3d_bias launch");
+    const convfuse::GenConv g{(int)k, (int)stride, 1};
+    return device_status(
+        convfuse::launch_conv3d_bias_generic(x, w, b, y, d, g, (hipStream_t)stream),
+        "conv3d_bias launch");
+}
+
+int mish_tanh(const float *v, float *y, int64_t count, void *stream)
+{
+    if (count < 0 || count > kMaxElems)
+        return fail(CONVFUSE_ERR_SHAPE, "mish_tanh: bad count=%lld", (long long)count);
+    if (count == 0) return CONVFUSE_OK;
+    if (!v || !y) return fail(CONVFUSE_ERR_NULL, "mish_tanh: v and y are required");
+    return device_status(convfuse::launch_mish_tanh(v, y, count, (hipStream_t)stream),
+                         "mish_tanh launch");
+}
+
+int div_maxpool_gap_bias_sum(const float *conv, float divisor, int64_t pool, const float *bias,
+                             float *out, int64_t N, int64_t C, int64_t OD, int64_t OH,
+                             int64_t OW, void *stream)
+{
+    const char *fn = "div_maxpool_gap_bias_sum";
+    if (N < 0 || N > kMaxDim || C <= 0 || C > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld C=%lld", fn, (long long)N, (long long)C);
+    if (!std::isfinite(divisor) || divisor == 0.0f)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: divisor must be finite and non-zero", fn);
+    int64_t PD, PH, PW;
+    if (!out_len(OD, pool, pool, 0, 1, &PD) || !out_len(OH, pool, pool, 0, 1, &PH) ||
+        !out_len(OW, pool, pool, 0, 1, &PW) || PD <= 0 || PH <= 0 || PW <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: pool=%lld does not fit %lldx%lldx%lld", fn,
+                    (long long)pool, (long long)OD, (long long)OH, (long long)OW);
+    if (!elems_ok({N, C, OD, OH, OW}) || !taps_ok(pool, 3))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (N == 0) return CONVFUSE_OK;
+    if (!conv || !bias || !out)
+        return fail(CONVFUSE_ERR_NULL, "%s: conv, bias and out are required", fn);
+    convfuse::PoolDims p{{N, 0, 0, 0, 0, C, OD, OH, OW, 0}, PD, PH, PW, divisor};
+    return device_status(convfuse::launch_div_maxpool_gap_bias_sum(conv, bias, out, p, (int)pool,
+                                                                   (hipStream_t)stream),
+                         "div_maxpool_gap_bias_sum launch");
+}
+
+int depthwise_conv2d(const float *x, const float *dw_w, const float *dw_b, float *y, int64_t N,
+                     int64_t C, int64_t H, int64_t W, int64_t K, int64_t stride, int64_t pad,
+                     int64_t dilation, void *stream)
+{
+    const char *fn = "depthwise_conv2d";
+    if (N < 0 || N > kMaxDim || C <= 0 || C > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld C=%lld", fn, (long long)N, (long long)C);
+    int64_t Ho, Wo;
+    if (!out_len(H, K, stride, pad, dilation, &Ho) || !out_len(W, K, stride, pad, dilation, &Wo) ||
+        Ho <= 0 || Wo <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: H=%lld W=%lld K=%lld stride=%lld pad=%lld "
+                    "dilation=%lld give no output", fn, (long long)H, (long long)W, (long long)K,
+                    (long long)stride, (long long)pad, (long long)dilation);
+    if (!elems_ok({N, C, H, W}) || !elems_ok({N, C, Ho, Wo}) || !elems_ok({C, K, K}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (!taps_ok(K, 2))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: K=%lld: more than 2^30 taps", fn, (long long)K);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !dw_w || !y) return fail(CONVFUSE_ERR_NULL, "%s: x, dw_w and y are required", fn);
+    convfuse::DwsepDims d{N, C, H, W, C, Ho, Wo, (int)pad};
+    const convfuse::GenConv g{(int)K, (int)stride, (int)dilation};
+    return device_status(
+        convfuse::launch_depthwise_conv2d(x, dw_w, dw_b, y, d, g, (hipStream_t)stream),
+        "depthwise_conv2d launch");
+}
+
+int pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y, int64_t N,
+                     int64_t Cin, int64_t H, int64_t W, int64_t Cout, void *stream)
+{
+    const char *fn = "pointwise_conv2d";
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim ||
+        H <= 0 || H > kMaxDim || W <= 0 || W > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld H=%lld W=%lld Cout=%lld", fn,
+                    (long long)N, (long long)Cin, (long long)H, (long long)W, (long long)Cout);
+    if (!elems_ok({N, Cin, H, W}) || !elems_ok({N, Cout, H, W}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !pw_w || !y) return fail(CONVFUSE_ERR_NULL, "%s: x, pw_w and y are required", fn);
+    convfuse::DwsepDims d{N, Cin, H, W, Cout, H, W, 1};
+    return device_status(
+        convfuse::launch_pointwise_conv2d(x, pw_w, pw_b, y, d, (hipStream_t)stream),
+        "pointwise_conv2d launch");
+}
+
 }  // extern "C"

@@ -191,7 +191,8 @@ struct ChunkStage {
 
 // ------------------------------------------------------------------ Mish/tanh epilogue
 // Wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns [ow0, ow0 + 16*NBW).
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
+// ACT: y = tanh(mish(conv + b)); otherwise y = conv + b (the unfused path's conv).
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool ACT>
 __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
@@ -252,7 +253,10 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) {
                     const int ow = ow0 + 16 * nb + (lane & 15);
-                    if (ow < d.OW) yrow[ow] = mish_tanh(acc[mb][nb][r] + bias);
+                    if (ow < d.OW) {
+                        const float v = acc[mb][nb][r] + bias;
+                        yrow[ow] = ACT ? mish_tanh(v) : v;
+                    }
                 }
             }
     } else {
@@ -414,17 +418,17 @@ inline bool vec_ok(const float *x, int64_t W) { return W % 4 == 0 && ((uintptr_t
 // 32-bit byte offsets over one staged chunk of CC input channels
 inline bool buf_ok(const Conv3dDims &d, int CC) { return 4 * CC * d.D * d.H * d.W <= kBufRange; }
 
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF>
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool ACT>
 void launch_act_kernel(const float *x, const float *w, const float *b, float *y,
                        const Conv3dDims &d, int64_t tiles, int64_t tw, int64_t th, int64_t td,
                        hipStream_t s)
 {
-    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF>),
+    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF, ACT>),
                        dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
                        (int)tw, (int)th, (int)td);
 }
 
-template <int MB, int NBW, int WD, int WH, int CC>
+template <int MB, int NBW, int WD, int WH, int CC, bool ACT>
 hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
                       const Conv3dDims &d, hipStream_t s)
 {
@@ -433,10 +437,10 @@ hipError_t launch_act(const float *x, const float *w, const float *b, float *y,
     const int64_t tiles = tw * th * td * d.N * og;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const bool v = vec_ok(x, d.W), bf = buf_ok(d, CC);
-    if (v && bf) launch_act_kernel<MB, NBW, WD, WH, CC, true, true>(x, w, b, y, d, tiles, tw, th, td, s);
-    else if (v) launch_act_kernel<MB, NBW, WD, WH, CC, true, false>(x, w, b, y, d, tiles, tw, th, td, s);
-    else if (bf) launch_act_kernel<MB, NBW, WD, WH, CC, false, true>(x, w, b, y, d, tiles, tw, th, td, s);
-    else launch_act_kernel<MB, NBW, WD, WH, CC, false, false>(x, w, b, y, d, tiles, tw, th, td, s);
+    if (v && bf) launch_act_kernel<MB, NBW, WD, WH, CC, true, true, ACT>(x, w, b, y, d, tiles, tw, th, td, s);
+    else if (v) launch_act_kernel<MB, NBW, WD, WH, CC, true, false, ACT>(x, w, b, y, d, tiles, tw, th, td, s);
+    else if (bf) launch_act_kernel<MB, NBW, WD, WH, CC, false, true, ACT>(x, w, b, y, d, tiles, tw, th, td, s);
+    else launch_act_kernel<MB, NBW, WD, WH, CC, false, false, ACT>(x, w, b, y, d, tiles, tw, th, td, s);
     return hipGetLastError();
 }
 
@@ -452,16 +456,33 @@ void launch_pool_kernel(const float *x, const float *w, const float *conv_b, flo
 
 }  // namespace
 
-hipError_t launch_conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
-                                   const Conv3dDims &d, hipStream_t s)
+namespace {
+
+template <bool ACT>
+hipError_t launch_conv3d(const float *x, const float *w, const float *b, float *y,
+                         const Conv3dDims &d, hipStream_t s)
 {
     const bool wide = d.OW > 16;
     if (d.O > 16) {
-        if (wide) return launch_act<4, 4, 2, 2, 4>(x, w, b, y, d, s);
-        return launch_act<4, 1, 2, 2, 4>(x, w, b, y, d, s);
+        if (wide) return launch_act<4, 4, 2, 2, 4, ACT>(x, w, b, y, d, s);
+        return launch_act<4, 1, 2, 2, 4, ACT>(x, w, b, y, d, s);
     }
-    if (wide) return launch_act<1, 4, 2, 2, 4>(x, w, b, y, d, s);
-    return launch_act<1, 1, 2, 2, 4>(x, w, b, y, d, s);
+    if (wide) return launch_act<1, 4, 2, 2, 4, ACT>(x, w, b, y, d, s);
+    return launch_act<1, 1, 2, 2, 4, ACT>(x, w, b, y, d, s);
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y,
+                                   const Conv3dDims &d, hipStream_t s)
+{
+    return launch_conv3d<true>(x, w, b, y, d, s);
+}
+
+hipError_t launch_conv3d_bias(const float *x, const float *w, const float *b, float *y,
+                              const Conv3dDims &d, hipStream_t s)
+{
+    return launch_conv3d<false>(x, w, b, y, d, s);
 }
 
 hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,

@@ -178,7 +178,9 @@ struct DwHaloStager {
 // pointwise weights of the chunk's first k-step, lane base applied (pw[cg*64*MB + mb] is the
 // operand of k-step cg, output block mb); dk: depthwise taps [c][12] (9 taps, bias at 9) of
 // the chunk's channel 4*cg + lane/16 at dk[cg*48].
-template <int MB, int R, int RS, int CS, int CC, bool PIXROWS>
+// DW = false: pointwise only (the unfused path's second pass); the operand is the staged
+// input itself, x at the centre tap of the K = 3, pad 1 halo.
+template <int MB, int R, int RS, int CS, int CC, bool PIXROWS, bool DW = true>
 __device__ __forceinline__ void dw_chunk(const float *xs, const float *pw, const float *dk,
                                          floatx4 (&acc)[MB][R])
 {
@@ -205,11 +207,14 @@ __device__ __forceinline__ void dw_chunk(const float *xs, const float *pw, const
             for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = xs[4 * cg * CS + hr * RS + kw];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float v = dbias;
+            float v = xv[r + 1][1];
+            if constexpr (DW) {
+                v = dbias;
 #pragma unroll
-            for (int kh = 0; kh < 3; ++kh)
+                for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
-                for (int kw = 0; kw < 3; ++kw) v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
+                    for (int kw = 0; kw < 3; ++kw) v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 if constexpr (PIXROWS)
@@ -375,7 +380,7 @@ constexpr size_t dw_weight_floats(int64_t C)
     return (size_t)(KS * 64 * MB + 4 * KS * 12 + 16 * MB);
 }
 
-template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS>
+template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS, bool DW>
 __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
         [&](int e) {
             const int c = e / 12, k = e - c * 12;
             float v = 0.0f;
-            if (c < C) {
+            if (DW && c < C) {
                 if (k < 9) v = dw_w[(int64_t)c * 9 + k];
                 else if (k == 9 && dw_b) v = dw_b[c];
             }
@@ -469,8 +474,8 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
                 lc = 0;
             }
             if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc);
-            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS>(xl, pl + (c0 / 4) * 64 * MB, dl + c0 * 12,
-                                                       acc);
+            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS, DW>(xl, pl + (c0 / 4) * 64 * MB,
+                                                           dl + c0 * 12, acc);
             if (last) break;
             lds_barrier();
             hs.store(xs, k);
@@ -501,7 +506,7 @@ struct DwWeightChunk {
     float dw;
 };
 
-template <int MB, int R, bool VEC, bool PIXROWS>
+template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
 __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
         }
         const int dc = c0 + tid / 12, dk = tid % 12;
         float v = 0.0f;
-        if (tid < DS && dc < C) {
+        if (DW && tid < DS && dc < C) {
             if (dk < 9) v = dw_w[(int64_t)dc * 9 + dk];
             else if (dk == 9 && dw_b) v = dw_b[dc];
         }
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
                 hs.load(k, x, d, n, h0, w0, c0 + kDwCC);
                 wload(wc, c0 + kDwCC);
             }
-            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS>(xl, pl, dl, acc);
+            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS, DW>(xl, pl, dl, acc);
         }
         dw_epilogue<MB, R, PIXROWS>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
     } else {
@@ -620,13 +625,13 @@ int cu_count()
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS>
+template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS, bool DW>
 hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_b,
                              const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
                              int obase, size_t lds, int per_cu, hipStream_t s)
 {
     using G = DwGeom<R, WH, CC>;
-    auto kern = dwsep_persistent_kernel<MB, R, WH, CC, VEC, PIXROWS>;
+    auto kern = dwsep_persistent_kernel<MB, R, WH, CC, VEC, PIXROWS, DW>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -642,7 +647,7 @@ hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_
     return hipGetLastError();
 }
 
-template <int MB, int R, bool VEC, bool PIXROWS>
+template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
 hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                           const float *pw_b, float *y, const DwsepDims &d, int obase,
                           hipStream_t s)
@@ -650,7 +655,7 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
     const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, R);
     const int64_t tiles = tw * th * d.N;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, PIXROWS>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, PIXROWS, DW>), dim3((unsigned)tiles),
                        dim3(256), 0, s, x, dw_w, dw_b, pw_w, pw_b, y, d, obase, tiles, (int)tw,
                        (int)th);
     return hipGetLastError();
@@ -660,7 +665,7 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
 // kernel with one 8-wave workgroup per CU and 32-channel chunks when its weights and halo fit
 // in LDS, else with 16-channel chunks (two 4-wave workgroups per CU, or one 8-wave one), else
 // the chunked kernel.
-template <int MB, int R, bool VEC, bool PIXROWS>
+template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
 hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                         const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
@@ -672,18 +677,18 @@ hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, co
     const bool small_planes =
         64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
     if (small_planes && lds_a <= kLdsBytes)
-        return launch_persistent<MB, R, 2, 32, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 2, 32, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_a, 1, s);
     if (small_planes && 2 * lds_b <= kLdsBytes)
-        return launch_persistent<MB, R, 1, 16, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 1, 16, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_b, 2, s);
     if (small_planes && lds_c <= kLdsBytes)
-        return launch_persistent<MB, R, 2, 16, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 2, 16, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_c, 1, s);
-    return launch_chunked<MB, 2, VEC, PIXROWS>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    return launch_chunked<MB, 2, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
 }
 
-template <int MB, int R>
+template <int MB, int R, bool DW>
 hipError_t launch(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                   const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
@@ -692,10 +697,29 @@ hipError_t launch(const float *x, const float *dw_w, const float *dw_b, const fl
     const bool vin = d.W % 4 == 0 && d.C % 4 == 0 && ((uintptr_t)x & 15) == 0 &&
                      ((uintptr_t)pw_w & 15) == 0;
     const bool vout = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
-    if (vin && vout) return launch_slice<MB, R, true, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    if (vin) return launch_slice<MB, R, true, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    if (vout) return launch_slice<MB, R, false, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    return launch_slice<MB, R, false, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vin && vout) return launch_slice<MB, R, true, true, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vin) return launch_slice<MB, R, true, false, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vout) return launch_slice<MB, R, false, true, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    return launch_slice<MB, R, false, false, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+}
+
+}  // namespace
+
+namespace {
+
+template <bool DW>
+hipError_t launch_all(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                      const float *pw_b, float *y, const DwsepDims &d, hipStream_t s)
+{
+    // One launch covers up to 192 output channels; wider layers run as several launches over
+    // consecutive output-channel slices (each rereads the input).
+    if (d.O <= 64) return launch<4, 4, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
+    if (d.O <= 128) return launch<8, 2, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
+    for (int64_t o0 = 0; o0 < d.O; o0 += 192) {
+        const hipError_t e = launch<12, 2, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, (int)o0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -704,15 +728,17 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
                                const float *pw_w, const float *pw_b, float *y,
                                const DwsepDims &d, hipStream_t s)
 {
-    // One launch covers up to 192 output channels; wider layers run as several launches over
-    // consecutive output-channel slices (each rereads the input).
-    if (d.O <= 64) return launch<4, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
-    if (d.O <= 128) return launch<8, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s);
-    for (int64_t o0 = 0; o0 < d.O; o0 += 192) {
-        const hipError_t e = launch<12, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, (int)o0, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_all<true>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
+}
+
+hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y,
+                                   const DwsepDims &d, hipStream_t s)
+{
+    DwsepDims p = d;
+    p.pad = 1;  // centre tap of the 3x3, pad 1 staging geometry: y has the input's H x W
+    p.Ho = d.H;
+    p.Wo = d.W;
+    return launch_all<false>(x, nullptr, nullptr, pw_w, pw_b, y, p, s);
 }
 
 }  // namespace convfuse

@@ -79,8 +79,9 @@ __device__ __forceinline__ void conv3d_direct(const float *__restrict__ x,
     }
 }
 
-// Wave tile t: (og, n, od, oh, owb) with owb fastest.
-template <int MB, int NB>
+// Wave tile t: (og, n, od, oh, owb) with owb fastest.  ACT: tanh(mish(conv + b)), else
+// conv + b.
+template <int MB, int NB, bool ACT>
 __global__ __launch_bounds__(64 * kGenWaves) void conv3d_mish_tanh_generic_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, GenConv g, int64_t tiles, int tiles_w)
@@ -111,7 +112,10 @@ __global__ __launch_bounds__(64 * kGenWaves) void conv3d_mish_tanh_generic_kerne
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int ow = ow0 + 16 * nb + (lane & 15);
-                if (ow < d.OW) yrow[ow] = mish_tanh(acc[mb][nb][r] + bias);
+                if (ow < d.OW) {
+                    const float v = acc[mb][nb][r] + bias;
+                    yrow[ow] = ACT ? mish_tanh(v) : v;
+                }
             }
         }
 }
@@ -278,9 +282,11 @@ inline hipError_t launch_waves(int64_t tiles, unsigned &grid)
 
 }  // namespace
 
-hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const float *b,
-                                           float *y, const Conv3dDims &d, const GenConv &g,
-                                           hipStream_t s)
+namespace {
+
+template <bool ACT>
+hipError_t launch_conv3d_generic(const float *x, const float *w, const float *b, float *y,
+                                 const Conv3dDims &d, const GenConv &g, hipStream_t s)
 {
     constexpr int NB = 2;
     const int64_t tw = cdiv(d.OW, 16 * NB);
@@ -288,15 +294,30 @@ hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const
     if (d.O > 32) {
         const int64_t tiles = cdiv(d.O, 64) * d.N * d.OD * d.OH * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
-        hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<4, NB>), dim3(grid),
+        hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<4, NB, ACT>), dim3(grid),
                            dim3(64 * kGenWaves), 0, s, x, w, b, y, d, g, tiles, (int)tw);
     } else {
         const int64_t tiles = cdiv(d.O, 16) * d.N * d.OD * d.OH * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
-        hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<1, NB>), dim3(grid),
+        hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<1, NB, ACT>), dim3(grid),
                            dim3(64 * kGenWaves), 0, s, x, w, b, y, d, g, tiles, (int)tw);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_mish_tanh_generic(const float *x, const float *w, const float *b,
+                                           float *y, const Conv3dDims &d, const GenConv &g,
+                                           hipStream_t s)
+{
+    return launch_conv3d_generic<true>(x, w, b, y, d, g, s);
+}
+
+hipError_t launch_conv3d_bias_generic(const float *x, const float *w, const float *b, float *y,
+                                      const Conv3dDims &d, const GenConv &g, hipStream_t s)
+{
+    return launch_conv3d_generic<false>(x, w, b, y, d, g, s);
 }
 
 namespace {

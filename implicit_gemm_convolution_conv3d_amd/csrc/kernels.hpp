@@ -48,6 +48,19 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
 hipError_t launch_conv3d_div_maxpool(const float *x, const float *w, const float *conv_b,
                                      float *y, const PoolDims &d, hipStream_t stream);
 
+// Unfused path: conv + bias written to y (tuned k = 3 / general), tanh(mish) elementwise,
+// the pooled channel sum from a stored conv output, depthwise alone, pointwise alone.
+hipError_t launch_conv3d_bias(const float *x, const float *w, const float *b, float *y,
+                              const Conv3dDims &d, hipStream_t stream);
+hipError_t launch_mish_tanh(const float *v, float *y, int64_t count, hipStream_t stream);
+hipError_t launch_div_maxpool_gap_bias_sum(const float *conv, const float *bias, float *out,
+                                           const PoolDims &d, int pool, hipStream_t stream);
+hipError_t launch_depthwise_conv2d(const float *x, const float *dw_w, const float *dw_b,
+                                   float *y, const DwsepDims &d, const GenConv &g,
+                                   hipStream_t stream);
+hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y,
+                                   const DwsepDims &d, hipStream_t stream);
+
 // out[n] = sum_c bias[c] (the constant term of the pooled channel sum), on the stream.
 hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
                                 hipStream_t stream);
@@ -64,6 +77,9 @@ hipError_t launch_conv3d_pool_sum_generic(const float *x, const float *w, const 
 hipError_t launch_conv3d_div_maxpool_generic(const float *x, const float *w,
                                              const float *conv_b, float *y, const PoolDims &d,
                                              const GenConv &g, int pool, hipStream_t stream);
+
+hipError_t launch_conv3d_bias_generic(const float *x, const float *w, const float *b, float *y,
+                                      const Conv3dDims &d, const GenConv &g, hipStream_t stream);
 
 hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const float *dw_b,
                                        const float *pw_w, const float *pw_b, float *y,

@@ -125,6 +125,42 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                  int64_t Cout, int64_t K, int64_t stride, int64_t pad, int64_t dilation,
                  void *stream);
 
+/*
+ * ---- Unfused path: the separate steps the fused entry points replace ----
+ * The pages' alternative to fusion runs the convolution as its own kernel, writes its output
+ * to memory, then applies the epilogue or the reduction in further kernels (page "Kimi-K2.6
+ * l2_p47": library conv + elementwise Mish/tanh; page "Kimi-K2.6 l2_p8": library conv +
+ * reduction kernel over its 441 MB output; page "Kimi-K2.6 l1_p86": separate depthwise and
+ * pointwise passes).  These entry points are those steps, built from the same kernels, so
+ * the saving of fusion can be measured.  Same conventions: device pointers, caller-owned
+ * buffers, the caller's stream, validation before any launch.
+ */
+
+/* y = conv3d(x, w) + b (b may be NULL), y [N][Cout][OD][OH][OW]; any k, stride, pad. */
+int conv3d_bias(const float *x, const float *w, const float *b, float *y,
+                int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                int64_t Cout, int64_t k, int64_t stride, int64_t pad, void *stream);
+
+/* y[i] = tanh(mish(v[i])) for i < count (v may equal y). */
+int mish_tanh(const float *v, float *y, int64_t count, void *stream);
+
+/* out[n] = sum_c ( mean(maxpool_pool(conv[n,c] / divisor)) + bias[c] ) from a stored conv
+ * output conv [N][C][OD][OH][OW] that already includes the conv bias; out [N] is
+ * initialised by the call.  Float atomics: the last bits may vary from run to run. */
+int div_maxpool_gap_bias_sum(const float *conv, float divisor, int64_t pool, const float *bias,
+                             float *out, int64_t N, int64_t C, int64_t OD, int64_t OH,
+                             int64_t OW, void *stream);
+
+/* y = depthwise K x K conv of x (+ dw_b), y [N][C][Ho][Wo] (the intermediate the fused
+ * dwsep_conv2d never writes). */
+int depthwise_conv2d(const float *x, const float *dw_w, const float *dw_b, float *y,
+                     int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t stride,
+                     int64_t pad, int64_t dilation, void *stream);
+
+/* y = pointwise 1x1 conv of x (+ pw_b), x [N][Cin][H][W] -> y [N][Cout][H][W]. */
+int pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y,
+                     int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout, void *stream);
+
 /* Output length of one spatial dimension, floor((in + 2*pad - dilation*(k-1) - 1)/stride)+1
  * (page l1_p86 output-size formula).  Pure host function.  Writes *out and returns
  * CONVFUSE_OK, or CONVFUSE_ERR_NULL / CONVFUSE_ERR_SHAPE (non-positive in, k, stride or

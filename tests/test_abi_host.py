@@ -149,3 +149,41 @@ def test_error_message_is_thread_local():
     assert seen["msg"] == ""
     assert seen["after"].startswith("dwsep_conv2d")
     assert cf.lib().convfuse_last_error().decode().startswith("conv3d_mish_tanh")
+
+
+@pytest.mark.parametrize("call,code,prefix", [
+    (lambda L: L.conv3d_bias(None, FAKE, None, FAKE, 1, 4, 8, 8, 8, 8, 3, 1, 0, None),
+     cf.ERR_NULL, "conv3d_bias"),
+    (lambda L: L.conv3d_bias(FAKE, FAKE, None, FAKE, 1, 0, 8, 8, 8, 8, 3, 1, 0, None),
+     cf.ERR_SHAPE, "conv3d_bias"),
+    (lambda L: L.conv3d_bias(FAKE, FAKE, None, FAKE, 1, 4, 2, 8, 8, 8, 3, 1, 0, None),
+     cf.ERR_SHAPE, "conv3d_bias"),
+    (lambda L: L.mish_tanh(None, FAKE, 10, None), cf.ERR_NULL, "mish_tanh"),
+    (lambda L: L.mish_tanh(FAKE, FAKE, -1, None), cf.ERR_SHAPE, "mish_tanh"),
+    (lambda L: L.div_maxpool_gap_bias_sum(FAKE, 0.0, 2, FAKE, FAKE, 1, 4, 8, 8, 8, None),
+     cf.ERR_SHAPE, "div_maxpool_gap_bias_sum"),
+    (lambda L: L.div_maxpool_gap_bias_sum(FAKE, 2.0, 9, FAKE, FAKE, 1, 4, 8, 8, 8, None),
+     cf.ERR_SHAPE, "div_maxpool_gap_bias_sum"),
+    (lambda L: L.div_maxpool_gap_bias_sum(FAKE, 2.0, 2, None, FAKE, 1, 4, 8, 8, 8, None),
+     cf.ERR_NULL, "div_maxpool_gap_bias_sum"),
+    (lambda L: L.depthwise_conv2d(FAKE, None, None, FAKE, 1, 4, 8, 8, 3, 1, 1, 1, None),
+     cf.ERR_NULL, "depthwise_conv2d"),
+    (lambda L: L.depthwise_conv2d(FAKE, FAKE, None, FAKE, 1, 4, 2, 8, 3, 1, 0, 1, None),
+     cf.ERR_SHAPE, "depthwise_conv2d"),
+    (lambda L: L.pointwise_conv2d(FAKE, None, None, FAKE, 1, 4, 8, 8, 8, None),
+     cf.ERR_NULL, "pointwise_conv2d"),
+    (lambda L: L.pointwise_conv2d(FAKE, FAKE, None, FAKE, 1, 4, 0, 8, 8, None),
+     cf.ERR_SHAPE, "pointwise_conv2d"),
+])
+def test_unfused_steps_validation(call, code, prefix):
+    assert call(cf.lib()) == code
+    assert cf.lib().convfuse_last_error().decode().startswith(prefix)
+
+
+def test_unfused_steps_empty_is_a_no_op():
+    L = cf.lib()
+    assert L.conv3d_bias(None, None, None, None, 0, 4, 8, 8, 8, 8, 3, 1, 0, None) == cf.OK
+    assert L.mish_tanh(None, None, 0, None) == cf.OK
+    assert L.div_maxpool_gap_bias_sum(None, 2.0, 2, None, None, 0, 4, 8, 8, 8, None) == cf.OK
+    assert L.depthwise_conv2d(None, None, None, None, 0, 4, 8, 8, 3, 1, 1, 1, None) == cf.OK
+    assert L.pointwise_conv2d(None, None, None, None, 0, 4, 8, 8, 8, None) == cf.OK
