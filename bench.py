@@ -39,7 +39,7 @@ def _olen(n, k, s=1, p=0, d=1):
 def out_dims(w):
     """Output spatial sizes of the convolution(s) of a workload."""
     d, p = w.dims, w.params
-    if w.op == "dwsep_conv2d":
+    if w.op.startswith("dwsep_conv2d"):
         args = (p["K"], p["stride"], p["pad"], p["dilation"])
         return _olen(d["H"], *args), _olen(d["W"], *args)
     s, pad = p.get("stride", 1), p.get("pad", 0)
@@ -156,8 +156,9 @@ def run_op(cf, w, t, out):
     elif w.op == "conv3d_div_maxpool":
         cf.conv3d_div_maxpool(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"], out=out)
     else:
-        cf.dwsep_conv2d(t["x"], t["dw_w"], t["dw_b"], t["pw_w"], t["pw_b"], p["stride"],
-                        p["pad"], p["dilation"], out=out)
+        fn = cf.dwsep_conv2d if w.op == "dwsep_conv2d" else cf.dwsep_conv2d_split_bf16
+        fn(t["x"], t["dw_w"], t["dw_b"], t["pw_w"], t["pw_b"], p["stride"], p["pad"],
+           p["dilation"], out=out)
 
 
 def out_shape(w):
@@ -375,7 +376,8 @@ def main():
     kname = {"conv3d_mish_tanh": "conv3d_mish_tanh_kernel",
              "conv3d_div_maxpool_gap_bias_sum": "conv3d_pool_sum_kernel",
              "conv3d_div_maxpool": "conv3d_pool_sum_kernel",
-             "dwsep_conv2d": "dwsep_persistent_kernel"}[dominant.op]
+             "dwsep_conv2d": "dwsep_persistent_kernel",
+             "dwsep_conv2d_split_bf16": "dwsep_split_kernel"}[dominant.op]
     achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),

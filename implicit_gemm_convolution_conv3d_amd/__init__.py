@@ -17,7 +17,7 @@ from . import _build
 __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
-    "pointwise_conv2d", "conv_out_len",
+    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv_out_len",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -28,7 +28,7 @@ _ERR_NAMES = {ERR_NULL: "NULL", ERR_SHAPE: "SHAPE", ERR_UNSUPPORTED: "UNSUPPORTE
 EXPORTED_SYMBOLS = (
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
-    "pointwise_conv2d",
+    "pointwise_conv2d", "dwsep_conv2d_split_bf16",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
 )
 
@@ -62,6 +62,7 @@ def lib():
             L.conv3d_div_maxpool.argtypes = (
                 [_vp] * 3 + [ctypes.c_float, _i64, _vp] + [_i64] * 7 + [_vp])
             L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
+            L.dwsep_conv2d_split_bf16.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
             L.conv3d_bias.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.mish_tanh.argtypes = [_vp, _vp, _i64, _vp]
             L.div_maxpool_gap_bias_sum.argtypes = (
@@ -169,7 +170,15 @@ def conv3d_div_maxpool(x, w, conv_b, divisor, pool, out=None):
     return out
 
 
-def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out=None):
+def dwsep_conv2d_split_bf16(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1,
+                            out=None):
+    """dwsep_conv2d with the pointwise GEMM as a three-term bf16 split of fp32 (opt-in)."""
+    return dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride, padding, dilation, out,
+                        _entry="dwsep_conv2d_split_bf16")
+
+
+def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out=None,
+                 _entry="dwsep_conv2d"):
     """y = pointwise(depthwise(x)); x [N,Cin,H,W], dw_w [Cin,1,K,K], pw_w [Cout,Cin,1,1]."""
     import torch
     N, C, H, W = x.shape
@@ -187,7 +196,7 @@ def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
-        _check(lib().dwsep_conv2d(_ptr(x, "x"), _ptr(dw_w, "dw_w"), _ptr(dw_b, "dw_b"),
+        _check(getattr(lib(), _entry)(_ptr(x, "x"), _ptr(dw_w, "dw_w"), _ptr(dw_b, "dw_b"),
                                   _ptr(pw_w, "pw_w"), _ptr(pw_b, "pw_b"), _ptr(out, "out", shp),
                                   N, C, H, W, O, K, stride, padding, dilation, _stream(x)))
     return out

@@ -246,6 +246,40 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                          "dwsep_conv2d launch");
 }
 
+int dwsep_conv2d_split_bf16(const float *x, const float *dw_w, const float *dw_b,
+                            const float *pw_w, const float *pw_b, float *y, int64_t N,
+                            int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t K,
+                            int64_t stride, int64_t pad, int64_t dilation, void *stream)
+{
+    const char *fn = "dwsep_conv2d_split_bf16";
+    if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
+                    (long long)Cin, (long long)Cout);
+    int64_t Ho, Wo;
+    if (!out_len(H, K, stride, pad, dilation, &Ho) || !out_len(W, K, stride, pad, dilation, &Wo) ||
+        Ho <= 0 || Wo <= 0)
+        return fail(CONVFUSE_ERR_SHAPE, "%s: H=%lld W=%lld K=%lld stride=%lld pad=%lld "
+                    "dilation=%lld give no output", fn, (long long)H, (long long)W, (long long)K,
+                    (long long)stride, (long long)pad, (long long)dilation);
+    if (!elems_ok({N, Cin, H, W}) || !elems_ok({N, Cout, Ho, Wo}) || !elems_ok({Cin, K, K}))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
+    if (!taps_ok(K, 2))
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: K=%lld: more than 2^30 taps", fn, (long long)K);
+    if (N == 0) return CONVFUSE_OK;
+    if (!x || !dw_w || !pw_w || !y)
+        return fail(CONVFUSE_ERR_NULL, "%s: x, dw_w, pw_w and y are required", fn);
+    convfuse::DwsepDims d{N, Cin, H, W, Cout, Ho, Wo, (int)pad};
+    if (K == 3 && stride == 1 && dilation == 1 && pad <= 2)
+        return device_status(convfuse::launch_dwsep_conv2d_split_bf16(x, dw_w, dw_b, pw_w, pw_b,
+                                                                      y, d, (hipStream_t)stream),
+                             "dwsep_conv2d_split_bf16 launch");
+    // other geometries run the fp32 general kernel (more accurate than the split contract)
+    const convfuse::GenConv g{(int)K, (int)stride, (int)dilation};
+    return device_status(convfuse::launch_dwsep_conv2d_generic(x, dw_w, dw_b, pw_w, pw_b, y, d, g,
+                                                               (hipStream_t)stream),
+                         "dwsep_conv2d_split_bf16 launch");
+}
+
 // ------------------------------------------------------------------ unfused path steps
 
 int conv3d_bias(const float *x, const float *w, const float *b, float *y, int64_t N,

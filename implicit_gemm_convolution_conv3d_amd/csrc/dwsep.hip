@@ -495,6 +495,205 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     }
 }
 
+// ----------------------------------------------------------------- split-bf16 kernel
+// Opt-in emulation of the fp32 pointwise GEMM on bf16 matrix cores: each fp32 operand v is
+// split into hi = bf16(v) (nearest) and lo = bf16(v - hi), and v*w is taken as
+// hi_v*hi_w + hi_v*lo_w + lo_v*hi_w with fp32 accumulation (the dropped lo*lo term and the
+// split residuals are below 2^-15 of |v*w|).  The depthwise step stays fp32 on the vector
+// ALUs.  One 16x16x32 bf16 k-step covers a 32-channel chunk: lane group g = lane/16 holds
+// the channels g + 4i (i = 0..7) of its pixel (A) or output channel (B), so the four groups
+// read four different LDS bank groups of the halo.  Same tiles, staging, prefetch and
+// epilogue as the persistent fp32 kernel.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)v[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(v[i] - (float)h);
+    }
+}
+
+// LDS bytes of the split kernel's weights: pointwise hi and lo fragments (KS k-steps of 32
+// channels x 64 lanes x MB, 16 bytes each), depthwise taps [32*KS][12], pointwise bias.
+template <int MB>
+constexpr size_t split_weight_bytes(int64_t C)
+{
+    const int64_t KS = (C + 31) / 32;
+    return (size_t)(2 * KS * 64 * MB * 16 + KS * 32 * 12 * 4 + 16 * MB * 4);
+}
+
+template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+__global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
+    const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
+    const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
+    DwsepDims d, int obase, int64_t tiles, int tiles_w, int tiles_h)
+{
+    constexpr int CC = 32;
+    using G = DwGeom<R, WH, CC>;
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    const int C = (int)d.C;  // small: the weights fit in LDS
+    const int KS = (C + CC - 1) / CC;
+    float *xs = dyn;
+    bf16x8 *pwh = reinterpret_cast<bf16x8 *>(dyn + G::XS);
+    bf16x8 *pwl = pwh + KS * 64 * MB;
+    float *dkall = reinterpret_cast<float *>(pwl + KS * 64 * MB);
+    float *bs = dkall + KS * 32 * 12;
+    const int ocnt = (int)(d.O - obase < 16 * MB ? d.O - obase : 16 * MB);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ww = wave & 3, wh = wave >> 2;
+
+    // Pointwise fragments: entry (s, l, mb) element i = pw[obase + 16mb + l%16][32s + l/16 + 4i]
+    for (int e = tid; e < KS * 64 * MB; e += G::NT) {
+        const int mb = e % MB, l = (e / MB) & 63, st = e / (64 * MB);
+        const int ol = 16 * mb + (l & 15);
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = 32 * st + (l >> 4) + 4 * i;
+            v[i] = (ol < ocnt && c < C) ? pw_w[(int64_t)(obase + ol) * C + c] : 0.0f;
+        }
+        bf16x8 hi, lo;
+        split_bf16(v, hi, lo);
+        pwh[e] = hi;
+        pwl[e] = lo;
+    }
+    lds_fill<G::NT, 4>(
+        dkall, KS * 32 * 12,
+        [&](int e) {
+            const int c = e / 12, k = e - c * 12;
+            float v = 0.0f;
+            if (c < C) {
+                if (k < 9) v = dw_w[(int64_t)c * 9 + k];
+                else if (k == 9 && dw_b) v = dw_b[c];
+            }
+            return v;
+        },
+        [](int e) { return e; });
+    if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
+
+    DwHaloStager<R, WH, CC, VEC, true> hs;
+    hs.init(tid, d.pad);
+    const int g = lane >> 4;
+    // lane bases: channel g of the chunk (channel g + 4i at + 4i*CS), pixel column
+    // 16*ww + lane%16, tap kw at LDS column + kw; depthwise taps of channel g (+ 48i)
+    const float *xl = xs + g * G::CS + R * wh * G::RS + 16 * ww + (lane & 15) + 4 - d.pad;
+    const float *dl = dkall + g * 12;
+
+    auto decode = [&](int64_t tile, int64_t &n, int &h0, int &w0) {
+        uint32_t t = (uint32_t)xcd_tile(tile, tiles);
+        const uint32_t tw = t % (uint32_t)tiles_w;
+        t /= (uint32_t)tiles_w;
+        const uint32_t th = t % (uint32_t)tiles_h;
+        n = t / (uint32_t)tiles_h;
+        h0 = (int)th * G::TH;
+        w0 = (int)tw * kDwTW;
+    };
+
+    // One chunk = one k-step: depthwise of the lane's 8 channels for each of its R rows,
+    // split, then three bf16 MFMAs per (output block, row).
+    auto chunk = [&](int st, floatx4 (&acc)[MB][R]) {
+        float dw[R][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float *xc = xl + 4 * i * G::CS;
+            const float *dk = dl + (32 * st + 4 * i) * 12;
+            const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dk);
+            const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dk + 4);
+            const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dk + 8);
+            const float kw9[9] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3], k2[0]};
+            float xv[R + 2][3];
+#pragma unroll
+            for (int hr = 0; hr < R + 2; ++hr)
+#pragma unroll
+                for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = xc[hr * G::RS + kw];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float v = k2[1];
+#pragma unroll
+                for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw) v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
+                dw[r][i] = v;
+            }
+        }
+        const bf16x8 *ph = pwh + (st * 64 + lane) * MB;
+        const bf16x8 *pl = pwl + (st * 64 + lane) * MB;
+        bf16x8 dhs[R], dls[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) split_bf16(dw[r], dhs[r], dls[r]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8 wh_ = ph[mb], wl_ = pl[mb];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const bf16x8 dh = dhs[r], dlo = dls[r];
+                if constexpr (PIXROWS) {
+                    acc[mb][r] = mfma_16x16x32_bf16(dlo, wh_, acc[mb][r]);
+                    acc[mb][r] = mfma_16x16x32_bf16(dh, wl_, acc[mb][r]);
+                    acc[mb][r] = mfma_16x16x32_bf16(dh, wh_, acc[mb][r]);
+                } else {
+                    acc[mb][r] = mfma_16x16x32_bf16(wh_, dlo, acc[mb][r]);
+                    acc[mb][r] = mfma_16x16x32_bf16(wl_, dh, acc[mb][r]);
+                    acc[mb][r] = mfma_16x16x32_bf16(wh_, dh, acc[mb][r]);
+                }
+            }
+        }
+    };
+
+    int64_t tile = blockIdx.x, n;
+    int h0, w0;
+    decode(tile, n, h0, w0);
+    DwHalo<R, WH, CC> k;
+    hs.load(k, x, d, n, h0, w0, 0);
+    lds_barrier();  // weights written; no wave reads the halo buffer yet
+    hs.store(xs, k);
+    lds_barrier();
+    floatx4 acc[MB][R];
+    for (;;) {
+        acc_init<MB, R, PIXROWS>(acc, bs);
+        const int64_t ntile = tile + gridDim.x;
+        int64_t nn = 0;
+        int nh0 = 0, nw0 = 0;
+        for (int c0 = 0;; c0 += CC) {
+            const bool last = c0 + CC >= C;
+            int64_t ln = n;
+            int lh = h0, lw = w0, lc = c0 + CC;
+            if (last) {
+                if (ntile < tiles) decode(ntile, nn, nh0, nw0);
+                ln = nn;
+                lh = nh0;
+                lw = nw0;
+                lc = 0;
+            }
+            if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc);
+            chunk(c0 / CC, acc);
+            if (last) break;
+            lds_barrier();
+            hs.store(xs, k);
+            lds_barrier();
+        }
+        float *tb = y + ((n * d.O + obase) * d.Ho + h0) * d.Wo;
+        dw_epilogue_buf<MB, R, PIXROWS>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
+                                        ocnt, acc);
+        if (ntile >= tiles) break;
+        tile = ntile;
+        n = nn;
+        h0 = nh0;
+        w0 = nw0;
+        lds_barrier();
+        hs.store(xs, k);
+        lds_barrier();
+    }
+}
+
 // ----------------------------------------------------------------- chunked kernel
 // One tile per workgroup (4 waves, R rows x 64 columns); pointwise weights (fragment order)
 // and depthwise taps of each chunk are staged with the chunk.
@@ -729,6 +928,71 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
                                const DwsepDims &d, hipStream_t s)
 {
     return launch_all<true>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
+}
+
+namespace {
+
+template <int MB, int R, bool VEC, bool PIXROWS>
+hipError_t launch_split_kernel(const float *x, const float *dw_w, const float *dw_b,
+                               const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
+                               int obase, size_t lds, hipStream_t s)
+{
+    using G = DwGeom<R, 2, 32>;
+    auto kern = dwsep_split_kernel<MB, R, 2, VEC, PIXROWS>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, G::TH);
+    const int64_t tiles = tw * th * d.N;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    int64_t grid = (int64_t)cu_count() / kNumXcd * kNumXcd;
+    if (grid < 1) grid = 1;
+    if (grid > tiles) grid = tiles;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), lds, s, x, dw_w, dw_b, pw_w, pw_b,
+                       y, d, obase, tiles, (int)tw, (int)th);
+    return hipGetLastError();
+}
+
+// Split-bf16 launch for output channels [obase, obase + 16*MB); false when it does not apply
+// (weights + halo above the LDS size, or byte offsets beyond 32 bits).
+template <int MB, int R>
+bool launch_split_slice(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
+                        const float *pw_b, float *y, const DwsepDims &d, int obase,
+                        hipStream_t s, hipError_t &err)
+{
+    const size_t lds = split_weight_bytes<MB>(d.C) + 4 * (size_t)DwGeom<R, 2, 32>::XS;
+    const bool small_planes =
+        64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
+    if (!small_planes || lds > kLdsBytes) return false;
+    const bool vin = d.W % 4 == 0 && ((uintptr_t)x & 15) == 0;
+    const bool vout = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
+    if (vin && vout) err = launch_split_kernel<MB, R, true, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    else if (vin) err = launch_split_kernel<MB, R, true, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    else if (vout) err = launch_split_kernel<MB, R, false, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    else err = launch_split_kernel<MB, R, false, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_dwsep_conv2d_split_bf16(const float *x, const float *dw_w, const float *dw_b,
+                                          const float *pw_w, const float *pw_b, float *y,
+                                          const DwsepDims &d, hipStream_t s)
+{
+    hipError_t err = hipSuccess;
+    bool done;
+    if (d.O <= 64) {
+        done = launch_split_slice<4, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s, err);
+    } else if (d.O <= 128) {
+        done = launch_split_slice<8, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, 0, s, err);
+    } else {
+        done = true;
+        for (int64_t o0 = 0; o0 < d.O && done && err == hipSuccess; o0 += 192)
+            done = launch_split_slice<12, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, (int)o0, s, err);
+    }
+    // Layers the split kernel does not cover run in fp32 (more accurate than asked for).
+    if (!done) return launch_all<true>(x, dw_w, dw_b, pw_w, pw_b, y, d, s);
+    return err;
 }
 
 hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y,

@@ -61,6 +61,12 @@ hipError_t launch_depthwise_conv2d(const float *x, const float *dw_w, const floa
 hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float *y,
                                    const DwsepDims &d, hipStream_t stream);
 
+// dwsep with the pointwise GEMM on bf16 matrix cores as a three-term split of each fp32
+// operand (opt-in precision mode; k = 3, stride 1, dilation 1, pad <= 2).
+hipError_t launch_dwsep_conv2d_split_bf16(const float *x, const float *dw_w, const float *dw_b,
+                                          const float *pw_w, const float *pw_b, float *y,
+                                          const DwsepDims &d, hipStream_t stream);
+
 // out[n] = sum_c bias[c] (the constant term of the pooled channel sum), on the stream.
 hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
                                 hipStream_t stream);

@@ -92,7 +92,7 @@ class Workload:
         if self.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
             return conv3d_pool_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                       self.params["k"], conv_bias=True)
-        if self.op == "dwsep_conv2d":
+        if self.op in ("dwsep_conv2d", "dwsep_conv2d_split_bf16"):
             return dwsep_inputs(s, d["N"], d["C"], d["H"], d["W"], d["O"], self.params["K"],
                                 bias=self.params["bias"])
         raise ValueError(self.op)
@@ -123,4 +123,12 @@ WORKLOADS = {
     # The pooling layer with its pooled tensor [N,O,7,31,31] as the output (no global mean).
     9: Workload(9, "conv3d_div_maxpool", "conv3d_div_maxpool",
                 dict(N=128, C=8, D=16, H=64, W=64, O=16), dict(k=3, divisor=2.0, pool=2)),
+    # The two depthwise-separable layers with the pointwise GEMM as a three-term bf16 split of
+    # fp32 on the matrix cores (opt-in precision mode with its own error contract).
+    10: Workload(10, "dwsep_conv2d_512_split_bf16", "dwsep_conv2d_split_bf16",
+                 dict(N=16, C=64, H=512, W=512, O=128),
+                 dict(K=3, stride=1, pad=1, dilation=1, bias=False)),
+    11: Workload(11, "dwsep_conv2d_333x517_bias_split_bf16", "dwsep_conv2d_split_bf16",
+                 dict(N=8, C=96, H=333, W=517, O=192),
+                 dict(K=3, stride=1, pad=1, dilation=1, bias=True)),
 }

@@ -126,6 +126,26 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                  void *stream);
 
 /*
+ * dwsep_conv2d with the pointwise GEMM on bf16 matrix cores (opt-in precision mode).  The
+ * pages weigh reduced-precision tensor-core formats (TF32) against true fp32 for these layers
+ * (page "Kimi-K2.6 l2_p47", the roofline estimate and the mma-precision paragraph); gfx950 has
+ * no TF32-like format, so fp32 is emulated: each operand v splits into hi = bf16(v) and
+ * lo = bf16(v - hi), and v*w is taken as hi*hi + hi*lo + lo*hi with fp32 accumulation.  The
+ * depthwise step, the biases and the accumulation stay fp32.
+ * Error contract (a separate one from the fp32 entry points): with bf16 rounding to nearest,
+ * |v - hi - lo| <= 2^-16 |v| and |lo| <= 2^-8 |v|, so each product is off by at most
+ * 3 * 2^-16 |v*w|.  Hence, with d[c] the depthwise output at the pixel,
+ *     |y[o] - y_exact[o]| <= 1e-4 + 1e-4 |y_exact[o]| + 2^-14 * sum_c |d[c] * pw[o,c]|.
+ * Same arguments, layouts and errors as dwsep_conv2d.  Applies to K = 3, stride 1,
+ * dilation 1, pad <= 2 when the layer's weights fit on chip; every other case runs the fp32
+ * kernels (which meet the tighter fp32 contract).
+ */
+int dwsep_conv2d_split_bf16(const float *x, const float *dw_w, const float *dw_b,
+                            const float *pw_w, const float *pw_b, float *y, int64_t N,
+                            int64_t Cin, int64_t H, int64_t W, int64_t Cout, int64_t K,
+                            int64_t stride, int64_t pad, int64_t dilation, void *stream);
+
+/*
  * ---- Unfused path: the separate steps the fused entry points replace ----
  * The pages' alternative to fusion runs the convolution as its own kernel, writes its output
  * to memory, then applies the epilogue or the reduction in further kernels (page "Kimi-K2.6

@@ -125,12 +125,32 @@ def test_dwsep_validation(kw, code):
     assert cf.lib().convfuse_last_error().decode().startswith("dwsep_conv2d")
 
 
+def call_dw_split(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W=8, O=8,
+                  K=3, s=1, p=1, d=1):
+    return cf.lib().dwsep_conv2d_split_bf16(x, dw, db, pw, pb, y, N, C, H, W, O, K, s, p, d, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(dw=None), cf.ERR_NULL), (dict(pw=None), cf.ERR_NULL),
+    (dict(y=None), cf.ERR_NULL), (dict(C=0), cf.ERR_SHAPE), (dict(O=0), cf.ERR_SHAPE),
+    (dict(N=-1), cf.ERR_SHAPE), (dict(H=0), cf.ERR_SHAPE), (dict(p=0, H=2), cf.ERR_SHAPE),
+    (dict(d=0), cf.ERR_SHAPE), (dict(s=0), cf.ERR_SHAPE), (dict(p=-1), cf.ERR_SHAPE),
+    (dict(s=1 << 25), cf.ERR_SHAPE), (dict(K=1 << 25), cf.ERR_SHAPE),
+    (dict(N=1 << 20, C=1 << 20, H=1 << 20), cf.ERR_SHAPE),
+    (dict(K=40000, p=20000, C=1, O=1), cf.ERR_UNSUPPORTED),
+])
+def test_dwsep_split_validation(kw, code):
+    assert call_dw_split(**kw) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("dwsep_conv2d_split_bf16")
+
+
 def test_empty_batch_is_a_no_op():
     # N = 0: nothing to compute, no pointer is needed and nothing is launched.
     assert call_act(x=None, w=None, y=None, N=0) == cf.OK
     assert call_pool(x=None, w=None, bias=None, out=None, N=0) == cf.OK
     assert call_maxpool(x=None, w=None, y=None, N=0) == cf.OK
     assert call_dw(x=None, dw=None, pw=None, y=None, N=0) == cf.OK
+    assert call_dw_split(x=None, dw=None, pw=None, y=None, N=0) == cf.OK
 
 
 def test_error_message_is_thread_local():

@@ -1,0 +1,148 @@
+"""GPU parity of dwsep_conv2d_split_bf16, the opt-in mode that runs the pointwise GEMM as a
+three-term bf16 split of fp32 on the matrix cores, against the fp64 CPU oracle through the
+C ABI.
+
+Its error contract is its own: with d[c] the exact depthwise output at the pixel,
+    |y[o] - y_exact[o]| <= 1e-4 + 1e-4 |y_exact[o]| + 2^-14 * sum_c |d[c] * pw[o,c]|
+(bf16 rounding to nearest leaves |v - hi - lo| <= 2^-16 |v| and |lo| <= 2^-8 |v|, so each
+product loses at most 3 * 2^-16 |v*w|).  The sum is computed here from the oracle's depthwise
+output (the oracle's depthwise-separable conv with an identity pointwise step).  Cases cover
+ragged tiles, channel counts off the 32-channel k-step, several output-channel slices, every
+padding the split kernel takes, the full-size workloads on sampled outputs, and a closed form
+that fixes which of the split's product terms are present."""
+import numpy as np
+import pytest
+
+import oracle
+from implicit_gemm_convolution_conv3d_amd import workloads as wl
+
+from test_gpu_parity import _torch, cf, dev, edge_indices, gather
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_SLACK = 2.0 ** -14
+
+
+def depthwise_exact(inp, stride, pad, dil):
+    """The depthwise output [N, C, Ho, Wo] in fp64 from the oracle (identity pointwise)."""
+    C = inp["dw_w"].shape[0]
+    eye = np.eye(C, dtype=np.float32).reshape(C, C, 1, 1)
+    return oracle.dwsep_conv2d(inp["x"], inp["dw_w"], inp["dw_b"], eye, None, stride, pad, dil)
+
+
+def assert_split_close(got, ref, abs_dot, what):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    bound = 1e-4 + 1e-4 * np.abs(ref) + SPLIT_SLACK * abs_dot
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    bad = err > bound
+    assert not bad.any(), "%s: %d/%d outside the split contract; worst err %.3g (bound %.3g)" % (
+        what, bad.sum(), bad.size, err.reshape(-1)[np.argmax(err / bound)],
+        bound.reshape(-1)[np.argmax(err / bound)])
+
+
+SPLIT_CASES = [
+    # (N, C, H, W, O, pad, bias)
+    (2, 8, 13, 70, 16, 1, False),          # ragged W and H tiles, one partial k-step
+    (1, 20, 9, 33, 40, 1, True),           # Cin % 4 != 0, Cout % 16 != 0
+    (1, 64, 17, 64, 128, 1, False),        # the 512^2 workload's channel shape
+    (1, 96, 7, 45, 192, 1, True),          # the odd workload's channel shape
+    (1, 40, 6, 20, 200, 2, True),          # padding 2, two output-channel slices
+    (1, 4, 5, 19, 8, 0, False),            # no padding
+    (1, 3, 1, 1, 5, 1, True),              # 1x1 image
+    (3, 33, 10, 24, 70, 1, True),          # one channel past a k-step, 3 images
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_split_small(case):
+    N, C, H, W, O, pad, bias = case
+    inp = wl.dwsep_inputs(700 + sum(case), N, C, H, W, O, bias=bias)
+    ref = oracle.dwsep_conv2d(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"], 1,
+                              pad, 1)
+    d = depthwise_exact(inp, 1, pad, 1)
+    abs_dot = np.einsum("oc,nchw->nohw", np.abs(inp["pw_w"][:, :, 0, 0].astype(np.float64)),
+                        np.abs(d))
+    y = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
+                                     dev(inp["pw_w"]), dev(inp["pw_b"]), 1, pad, 1)
+    assert tuple(y.shape) == ref.shape
+    assert_split_close(y.cpu().numpy(), ref, abs_dot, "split %s" % (case,))
+
+
+def test_split_general_parameters_run_fp32():
+    """Geometries outside the split kernel (here K = 5, stride 2) run the fp32 kernels and meet
+    the fp32 tolerance."""
+    inp = wl.dwsep_inputs(790, 1, 12, 20, 41, 24, K=5, bias=True)
+    ref = oracle.dwsep_conv2d(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"], 2, 2,
+                              1)
+    y = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
+                                     dev(inp["pw_w"]), dev(inp["pw_b"]), 2, 2, 1)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-4 + 1e-4 * np.abs(ref))
+
+
+def test_split_terms_closed_form():
+    """Depthwise output d = 1 + 2^-10 everywhere (centre tap 1 + 2^-10 on an all-ones image)
+    and pointwise weights w = 1 + 2^-10: hi = 1 and lo = 2^-10 for both, so the three-term
+    product is exactly 1 + 2^-9 (the dropped lo*lo term is 2^-20) and each output is
+    C (1 + 2^-9), against C (1 + 2^-9 + 2^-20) exactly.  A plain bf16 product would give C."""
+    torch = _torch()
+    N, C, H, W, O = 1, 32, 6, 70, 16
+    e = 2.0 ** -10
+    x = torch.ones((N, C, H, W), device="cuda")
+    dw = torch.zeros((C, 1, 3, 3), device="cuda")
+    dw[:, 0, 1, 1] = 1.0 + e
+    pw = torch.full((O, C, 1, 1), 1.0 + e, device="cuda")
+    y = cf().dwsep_conv2d_split_bf16(x, dw, None, pw, None, 1, 1, 1)
+    assert bool((y == C * (1.0 + 2 * e)).all()), y.unique()
+    y32 = cf().dwsep_conv2d(x, dw, None, pw, None, 1, 1, 1)
+    exact = C * (1.0 + 2 * e + e * e)
+    assert float((y32 - exact).abs().max()) <= 1e-4 + 1e-4 * exact
+
+
+@pytest.mark.parametrize("index", [10, 11])
+def test_split_full_workload_sampled(index):
+    w = wl.WORKLOADS[index]
+    inp = w.inputs()
+    p = w.params
+    args = (p["stride"], p["pad"], p["dilation"])
+    y = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
+                                     dev(inp["pw_w"]), dev(inp["pw_b"]), *args)
+    dd = w.dims
+    assert tuple(y.shape) == (dd["N"], dd["O"], dd["H"], dd["W"])
+    rng = np.random.default_rng(31 + index)
+    idx = edge_indices(y.shape, rng, 6000)
+    ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
+                                 idx, *args)
+    # depthwise outputs of every channel at the sampled pixels
+    n, o, h, ww = np.unravel_index(idx, y.shape)
+    C = dd["C"]
+    cs = np.arange(C)
+    didx = np.ravel_multi_index((np.repeat(n, C), np.tile(cs, idx.size), np.repeat(h, C),
+                                 np.repeat(ww, C)), (dd["N"], C, dd["H"], dd["W"]))
+    eye = np.eye(C, dtype=np.float32).reshape(C, C, 1, 1)
+    d = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], eye, None, didx,
+                               *args).reshape(idx.size, C)
+    pw = np.abs(inp["pw_w"][:, :, 0, 0].astype(np.float64))
+    abs_dot = np.einsum("sc,sc->s", pw[o], np.abs(d))
+    assert_split_close(gather(y, idx), ref, abs_dot, "split workload %d sampled" % index)
+    torch = _torch()
+    assert bool(torch.isfinite(y).all())
+    # the split kernel ran (its rounding differs from the fp32 kernel's) and is deterministic
+    y32 = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
+                            dev(inp["pw_b"]), *args)
+    assert not bool(torch.equal(y, y32))
+    y2 = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
+                                      dev(inp["pw_w"]), dev(inp["pw_b"]), *args)
+    assert bool(torch.equal(y, y2))
+
+
+def test_split_not_written_past_end():
+    torch = _torch()
+    inp = wl.dwsep_inputs(791, 1, 5, 7, 21, 19, bias=True)
+    n_out = 19 * 7 * 21
+    buf = torch.full((n_out + 4096,), 12345.0, device="cuda")
+    y = buf[:n_out].view(1, 19, 7, 21)
+    cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
+                                 dev(inp["pw_w"]), dev(inp["pw_b"]), 1, 1, 1, out=y)
+    assert bool((buf[n_out:] == 12345.0).all())
