@@ -7,6 +7,7 @@
 namespace convfuse {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;   // CDNA wavefront width
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each

@@ -105,8 +105,10 @@ __device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
 
 // One chunk of the K loop: 27 taps x CC/4 channel groups.  The NB voxel blocks of the wave
 // sit at LDS offsets boff[] from the lane base; acc[mb][nb] accumulates output channels
-// 16*mb.. of block nb.
-template <int MB, int NB, int CC, int HH, int RS, int CS>
+// 16*mb.. of block nb.  VROWS: the voxels are the MFMA's rows (A operand) and each lane ends
+// with 4 consecutive voxels of one output channel; otherwise 4 output channels of one voxel.
+// (The lane's operand values are the same either way: only the roles of A and B swap.)
+template <int MB, int NB, int CC, int HH, int RS, int CS, bool VROWS = false>
 __device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
                                             const float *__restrict__ ws, int xlane,
                                             const int (&boff)[NB], floatx4 (&acc)[MB][NB])
@@ -131,7 +133,8 @@ __device__ __forceinline__ void igemm_chunk(const float *__restrict__ xs,
                     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb)
-                            acc[mb][nb] = mfma_16x16x4(a[mb], bv[nb], acc[mb][nb]);
+                            acc[mb][nb] = VROWS ? mfma_16x16x4(bv[nb], a[mb], acc[mb][nb])
+                                                : mfma_16x16x4(a[mb], bv[nb], acc[mb][nb]);
                 }
 }
 
@@ -192,7 +195,10 @@ struct ChunkStage {
 // ------------------------------------------------------------------ Mish/tanh epilogue
 // Wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns [ow0, ow0 + 16*NBW).
 // ACT: y = tanh(mish(conv + b)); otherwise y = conv + b (the unfused path's conv).
-template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool ACT>
+// The voxels are the MFMA rows, so each lane ends with 4 consecutive voxels of one output
+// channel, stored with SW-float stores (SW = 2 needs 8-byte aligned output rows, SW = 4
+// 16-byte aligned ones).
+template <int MB, int NBW, int WD, int WH, int CC, bool VEC, bool BUF, bool ACT, int SW>
 __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
@@ -240,25 +246,45 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
             stage.store(xs, ws, d.pad);
             __syncthreads();
             if (c0 + CC < d.C) stage.load(x, w, d, n, c0 + CC, o0, id0, ih0, ow0);
-            igemm_chunk<MB, NBW, CC, HH, RS, CS>(xs, ws, xlane, boff, acc);
+            igemm_chunk<MB, NBW, CC, HH, RS, CS, true>(xs, ws, xlane, boff, acc);
         }
+        {
+            // lane holds columns ow0 + 16*nb + 4*(lane/16) + 0..3 of output channel
+            // o0 + 16*mb + lane%16
+            const int j = lane & 15, q = 4 * (lane >> 4);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+            for (int mb = 0; mb < MB; ++mb) {
+                const int o = o0 + 16 * mb + j;
                 if (o >= d.O) continue;
                 const float bias = b ? b[o] : 0.0f;
                 float *yrow = y + (((n * d.O + o) * d.OD + od) * d.OH + oh) * d.OW;
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb) {
-                    const int ow = ow0 + 16 * nb + (lane & 15);
-                    if (ow < d.OW) {
-                        const float v = acc[mb][nb][r] + bias;
-                        yrow[ow] = ACT ? mish_tanh(v) : v;
+                    const int ow = ow0 + 16 * nb + q;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float a = acc[mb][nb][r] + bias;
+                        v[r] = ACT ? mish_tanh(a) : a;
+                    }
+                    if (ow + 3 < d.OW) {
+                        if constexpr (SW == 4) {
+                            *reinterpret_cast<floatx4 *>(yrow + ow) = floatx4{v[0], v[1], v[2], v[3]};
+                        } else if constexpr (SW == 2) {
+                            *reinterpret_cast<floatx2 *>(yrow + ow) = floatx2{v[0], v[1]};
+                            *reinterpret_cast<floatx2 *>(yrow + ow + 2) = floatx2{v[2], v[3]};
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) yrow[ow + r] = v[r];
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (ow + r < d.OW) yrow[ow + r] = v[r];
                     }
                 }
             }
+        }
     } else {
         // This wave's row lies past the output: it only helps stage the shared tiles.
         for (int c0 = 0; c0 < d.C; c0 += CC) {
@@ -423,9 +449,16 @@ void launch_act_kernel(const float *x, const float *w, const float *b, float *y,
                        const Conv3dDims &d, int64_t tiles, int64_t tw, int64_t th, int64_t td,
                        hipStream_t s)
 {
-    hipLaunchKernelGGL((conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF, ACT>),
-                       dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d, tiles,
-                       (int)tw, (int)th, (int)td);
+    // widest output stores the rows' alignment allows
+    const uintptr_t ya = (uintptr_t)y;
+    const int sw = (d.OW % 4 == 0 && (ya & 15) == 0) ? 4 : (d.OW % 2 == 0 && (ya & 7) == 0) ? 2 : 1;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d,
+                           tiles, (int)tw, (int)th, (int)td);
+    };
+    if (sw == 4) go(conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF, ACT, 4>);
+    else if (sw == 2) go(conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF, ACT, 2>);
+    else go(conv3d_mish_tanh_kernel<MB, NBW, WD, WH, CC, VEC, BUF, ACT, 1>);
 }
 
 template <int MB, int NBW, int WD, int WH, int CC, bool ACT>
