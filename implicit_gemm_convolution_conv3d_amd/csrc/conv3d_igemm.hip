@@ -20,88 +20,11 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "conv3d_tile.hpp"
 
 namespace convfuse {
 
 namespace {
-
-// Weights of output channels [o0, o0 + 16*MB) x input channels [c0, c0 + CC), all 27 taps,
-// held in registers between the global load and the LDS store.
-// LDS layout (A-fragment order): ws[((tap*CC/4 + cg)*64 + lane)*MB + mb] holds
-// w[o0 + 16*mb + lane%16][c0 + 4*cg + lane/16][tap].  Missing channels are zero.
-// Pair p = (cl*16 + j)*MB + mb names output channel 16*mb + j and input channel cl; its slot
-// at tap t is t*(CC/4)*64*MB + p, so threads holding consecutive pairs write consecutive LDS
-// words.  A pair's 27 taps are contiguous in memory.  With at least as many pairs as
-// threads, thread t owns the pairs t, t + NT, ...; with fewer, pair t % PAIRS is split over
-// TPP threads, TPT taps each.
-template <int MB, int CC, int NT>
-struct WeightChunk {
-    static constexpr int PAIRS = 16 * MB * CC;
-    static constexpr int TPP = PAIRS >= NT ? 1 : NT / PAIRS;  // threads per pair
-    static constexpr int TPT = (27 + TPP - 1) / TPP;          // taps per thread
-    static constexpr int PP = (PAIRS * TPP + NT - 1) / NT;
-    static constexpr int TAPSTRIDE = (CC / 4) * 64 * MB;
-    static_assert(PAIRS >= NT || NT % PAIRS == 0, "pair split");
-    float v[PP][TPT];
-
-    __device__ __forceinline__ static void decode(int idx, int &pair, int &t0)
-    {
-        if constexpr (TPP == 1) {
-            pair = idx;
-            t0 = 0;
-        } else {
-            pair = idx % PAIRS;
-            t0 = (idx / PAIRS) * TPT;
-        }
-    }
-
-    __device__ __forceinline__ void load(const float *__restrict__ w, const Conv3dDims &d, int o0,
-                                         int c0)
-    {
-#pragma unroll
-        for (int p = 0; p < PP; ++p) {
-            int pair, t0;
-            decode(threadIdx.x + p * NT, pair, t0);
-            const int mb = pair % MB, jj = (pair / MB) % 16, cl = pair / (16 * MB);
-            const int o = o0 + 16 * mb + jj, c = c0 + cl;
-            const bool ok = pair < PAIRS && o < d.O && c < d.C;
-            const float *src = w + ((int64_t)o * d.C + c) * 27 + t0;
-#pragma unroll
-            for (int i = 0; i < TPT; ++i) v[p][i] = ok && t0 + i < 27 ? src[i] : 0.0f;
-        }
-    }
-
-    __device__ __forceinline__ void store(float *__restrict__ ws) const
-    {
-#pragma unroll
-        for (int p = 0; p < PP; ++p) {
-            int pair, t0;
-            decode(threadIdx.x + p * NT, pair, t0);
-            if (pair >= PAIRS) continue;
-#pragma unroll
-            for (int i = 0; i < TPT; ++i)
-                if (t0 + i < 27) ws[(t0 + i) * TAPSTRIDE + pair] = v[p][i];
-        }
-    }
-};
-
-template <int MB>
-__device__ __forceinline__ void load_afrag(const float *p, float (&a)[MB])
-{
-    if constexpr (MB % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < MB / 4; ++i) {
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(p + 4 * i);
-            a[4 * i + 0] = v[0];
-            a[4 * i + 1] = v[1];
-            a[4 * i + 2] = v[2];
-            a[4 * i + 3] = v[3];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) a[i] = p[i];
-    }
-}
 
 // One chunk of the K loop: 27 taps x CC/4 channel groups.  The NB voxel blocks of the wave
 // sit at LDS offsets boff[] from the lane base; acc[mb][nb] accumulates output channels
@@ -148,7 +71,7 @@ struct ChunkStage {
     using Halo = std::conditional_t<BUF, BufHaloRows<CC * HD * HH, MAIN, NT, VEC>,
                                     HaloRows<CC * HD * HH, MAIN, NT, VEC>>;
     Halo halo;
-    WeightChunk<MB, CC, NT> wts;
+    WeightChunk<MB, CC, NT, 27> wts;
 
     __device__ __forceinline__ void load(const float *__restrict__ x, const float *__restrict__ w,
                                          const Conv3dDims &d, int64_t n, int c0, int o0, int id0,
@@ -176,7 +99,7 @@ struct ChunkStage {
             };
             halo.load(src, iw0, d.pad, (int)d.W);
         }
-        wts.load(w, d, o0, c0);
+        wts.load(w, d, o0, c0, 27, 0);
     }
 
     __device__ __forceinline__ void store(float *__restrict__ xs, float *__restrict__ ws,
@@ -248,43 +171,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
             if (c0 + CC < d.C) stage.load(x, w, d, n, c0 + CC, o0, id0, ih0, ow0);
             igemm_chunk<MB, NBW, CC, HH, RS, CS, true>(xs, ws, xlane, boff, acc);
         }
-        {
-            // lane holds columns ow0 + 16*nb + 4*(lane/16) + 0..3 of output channel
-            // o0 + 16*mb + lane%16
-            const int j = lane & 15, q = 4 * (lane >> 4);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int o = o0 + 16 * mb + j;
-                if (o >= d.O) continue;
-                const float bias = b ? b[o] : 0.0f;
-                float *yrow = y + (((n * d.O + o) * d.OD + od) * d.OH + oh) * d.OW;
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) {
-                    const int ow = ow0 + 16 * nb + q;
-                    float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float a = acc[mb][nb][r] + bias;
-                        v[r] = ACT ? mish_tanh(a) : a;
-                    }
-                    if (ow + 3 < d.OW) {
-                        if constexpr (SW == 4) {
-                            *reinterpret_cast<floatx4 *>(yrow + ow) = floatx4{v[0], v[1], v[2], v[3]};
-                        } else if constexpr (SW == 2) {
-                            *reinterpret_cast<floatx2 *>(yrow + ow) = floatx2{v[0], v[1]};
-                            *reinterpret_cast<floatx2 *>(yrow + ow + 2) = floatx2{v[2], v[3]};
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) yrow[ow + r] = v[r];
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (ow + r < d.OW) yrow[ow + r] = v[r];
-                    }
-                }
-            }
-        }
+        store_conv_row<MB, NBW, ACT, SW>(y, b, d, n, od, oh, ow0, o0, acc);
     } else {
         // This wave's row lies past the output: it only helps stage the shared tiles.
         for (int c0 = 0; c0 < d.C; c0 += CC) {
@@ -449,9 +336,7 @@ void launch_act_kernel(const float *x, const float *w, const float *b, float *y,
                        const Conv3dDims &d, int64_t tiles, int64_t tw, int64_t th, int64_t td,
                        hipStream_t s)
 {
-    // widest output stores the rows' alignment allows
-    const uintptr_t ya = (uintptr_t)y;
-    const int sw = (d.OW % 4 == 0 && (ya & 15) == 0) ? 4 : (d.OW % 2 == 0 && (ya & 7) == 0) ? 2 : 1;
+    const int sw = conv_store_width(y, d.OW);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d,
                            tiles, (int)tw, (int)th, (int)td);

@@ -7,13 +7,16 @@
 // padding of the Conv3d; page "Kimi-K2.6 l1_p86", stride/padding/dilation and kernel sizes
 // 1/3/5/7 of the depthwise-separable Conv2d; page "Kimi-K2.6 l2_p8", the pooled channel sum).
 //
-// Each is a direct implicit GEMM over global memory: one wave owns 16*MB output channels x
-// 16*NB output positions along W, and each 16x16x4 MFMA k-step gathers its operands straight
-// from global memory (L1/L2 serve the reuse) with zero padding by bounds checks.  There is
-// no LDS staging and no inter-wave synchronisation except the pooled sum's window reduction.
+// Conv3d with kernel size 3, 5 or 7 and stride 1 or 2 (any padding) runs an LDS-staged
+// implicit GEMM with the tuned kernel's organisation (conv3d_staged_kernel).  Everything else
+// is a direct implicit GEMM over global memory: one wave owns 16*MB output channels x 16*NB
+// output positions along W, and each 16x16x4 MFMA k-step gathers its operands straight from
+// global memory (L1/L2 serve the reuse) with zero padding by bounds checks; there is no LDS
+// staging and no inter-wave synchronisation except the pooled sum's window reduction.
 // The GEMM K order is tap-major, input-channel-minor: a k-step is four input channels at one
 // tap, lane l supplying input channel 4*cg + l/16.
 #include "common.hpp"
+#include "conv3d_tile.hpp"
 #include "kernels.hpp"
 
 namespace convfuse {
@@ -77,6 +80,151 @@ __device__ __forceinline__ void conv3d_direct(const float *__restrict__ x,
             }
         }
     }
+}
+
+// ------------------------------------------------------------------ staged general Conv3d
+// Workgroup = 2 x 2 waves; wave (wd, wh) owns output row (od0 + wd, oh0 + wh), columns
+// [ow0, ow0 + 16*NBW) and output channels [o0, o0 + 16*MB).  The K loop runs over chunks of
+// four input channels at one kernel depth kd.  Per channel and per output depth of the tile a
+// chunk stages the HHR input rows that the tile's two output rows reach, COLS columns each
+// (the columns its 16*NBW outputs reach), plus the chunk's K*K taps of weights in A-fragment
+// order.  The next chunk is loaded into registers while the current one computes.
+template <int K, int S, int NBW>
+struct StagedGeom {
+    static constexpr int WD = 2, WH = 2, NT = 64 * WD * WH;
+    static constexpr int HHR = (WH - 1) * S + K;          // input rows per (channel, depth)
+    static constexpr int COLS = (16 * NBW - 1) * S + K;   // input columns per row
+    static constexpr int RS = round_up(COLS, 4);
+    static constexpr int CS = halo_channel_stride(WD * HHR * RS);
+    static constexpr int XS = 4 * CS;
+    static constexpr int ROWS = 4 * WD * HHR;             // staged rows per chunk
+    static constexpr int RPW = (ROWS + 3) / 4;            // rows per wave
+    static constexpr int CPL = (COLS + 63) / 64;          // columns per lane
+};
+
+// Input rows of one chunk in registers between global load and LDS store.  Wave w handles
+// rows r = w + 4i: channel r / (WD*HHR), tile depth (r / HHR) % WD, row r % HHR; lane l
+// columns l + 64j.  LDS column c holds input column ow0*S - pad + c.
+template <int K, int S, int NBW>
+struct StagedHalo {
+    using G = StagedGeom<K, S, NBW>;
+    float v[G::RPW][G::CPL];
+
+    __device__ __forceinline__ void load(const float *__restrict__ x, const Conv3dDims &d,
+                                         int64_t n, int c0, int kd, int od0, int oh0, int ow0)
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int iw0 = ow0 * S - d.pad;
+#pragma unroll
+        for (int i = 0; i < G::RPW; ++i) {
+            const int r = wave + 4 * i;
+            const int cl = r / (G::WD * G::HHR), rem = r % (G::WD * G::HHR);
+            const int wdp = rem / G::HHR, hr = rem % G::HHR;
+            const int c = c0 + cl, id = (od0 + wdp) * S - d.pad + kd, ih = oh0 * S - d.pad + hr;
+            const bool rowok = r < G::ROWS && c < d.C && (unsigned)id < (unsigned)d.D &&
+                               (unsigned)ih < (unsigned)d.H;
+            const float *src =
+                x + (((n * d.C + (rowok ? c : 0)) * d.D + (rowok ? id : 0)) * d.H +
+                     (rowok ? ih : 0)) * d.W;
+#pragma unroll
+            for (int jj = 0; jj < G::CPL; ++jj) {
+                const int col = lane + 64 * jj, iw = iw0 + col;
+                v[i][jj] = rowok && col < G::COLS && (unsigned)iw < (unsigned)d.W ? src[iw] : 0.0f;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float *__restrict__ xs) const
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < G::RPW; ++i) {
+            const int r = wave + 4 * i;
+            if (r >= G::ROWS) continue;
+            const int cl = r / (G::WD * G::HHR), rem = r % (G::WD * G::HHR);
+            const int wdp = rem / G::HHR, hr = rem % G::HHR;
+            float *dst = xs + cl * G::CS + (wdp * G::HHR + hr) * G::RS;
+#pragma unroll
+            for (int jj = 0; jj < G::CPL; ++jj) {
+                const int col = lane + 64 * jj;
+                if (col < G::COLS) dst[col] = v[i][jj];
+            }
+        }
+    }
+};
+
+// One chunk: K*K taps of one k-step each (four channels); voxels are the MFMA rows.
+template <int MB, int NBW, int K, int S>
+__device__ __forceinline__ void staged_chunk(const float *__restrict__ xs,
+                                             const float *__restrict__ ws, int xlane,
+                                             floatx4 (&acc)[MB][NBW])
+{
+    using G = StagedGeom<K, S, NBW>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+            float a[MB];
+            load_afrag<MB>(ws + ((kh * K + kw) * 64 + lane) * MB, a);
+            float bv[NBW];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) bv[nb] = xs[xlane + kh * G::RS + kw + 16 * S * nb];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+                    acc[mb][nb] = mfma_16x16x4(bv[nb], a[mb], acc[mb][nb]);
+        }
+}
+
+template <int MB, int NBW, int K, int S, bool ACT, int SW>
+__global__ __launch_bounds__(256, 2) void conv3d_staged_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
+    float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
+{
+    using G = StagedGeom<K, S, NBW>;
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    float *xs = dyn;
+    float *ws = dyn + G::XS;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w); t /= tiles_w;
+    const int th = (int)(t % tiles_h); t /= tiles_h;
+    const int td = (int)(t % tiles_d); t /= tiles_d;
+    const int64_t n = t % d.N;
+    const int og = (int)(t / d.N);
+    const int od0 = td * G::WD, oh0 = th * G::WH, ow0 = tw * 16 * NBW, o0 = og * 16 * MB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wd = wave / G::WH, wh = wave % G::WH;
+    const int xlane = (lane >> 4) * G::CS + (wd * G::HHR + wh * S) * G::RS + (lane & 15) * S;
+
+    StagedHalo<K, S, NBW> halo;
+    WeightChunk<MB, 4, G::NT, K * K> wts;
+    const int chunks = (int)((d.C + 3) / 4) * K;  // chunk q: channels 4*(q/K).., depth q%K
+    auto load = [&](int q) {
+        const int c0 = (q / K) * 4, kd = q % K;
+        halo.load(x, d, n, c0, kd, od0, oh0, ow0);
+        wts.load(w, d, o0, c0, K * K * K, kd * K * K);
+    };
+    load(0);
+    const int od = od0 + wd, oh = oh0 + wh;
+    const bool active = od < d.OD && oh < d.OH;
+    floatx4 acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < chunks; ++q) {
+        __syncthreads();
+        halo.store(xs);
+        wts.store(ws);
+        __syncthreads();
+        if (q + 1 < chunks) load(q + 1);
+        // (a wave whose row lies past the output only helps stage the shared tiles)
+        if (active) staged_chunk<MB, NBW, K, S>(xs, ws, xlane, acc);
+    }
+    if (active) store_conv_row<MB, NBW, ACT, SW>(y, b, d, n, od, oh, ow0, o0, acc);
 }
 
 // Wave tile t: (og, n, od, oh, owb) with owb fastest.  ACT: tanh(mish(conv + b)), else
@@ -284,10 +432,53 @@ inline hipError_t launch_waves(int64_t tiles, unsigned &grid)
 
 namespace {
 
+template <int MB, int NBW, int K, int S, bool ACT, int SW>
+hipError_t launch_staged_sw(const float *x, const float *w, const float *b, float *y,
+                            const Conv3dDims &d, hipStream_t s)
+{
+    using G = StagedGeom<K, S, NBW>;
+    auto kern = conv3d_staged_kernel<MB, NBW, K, S, ACT, SW>;
+    const size_t lds = 4 * (size_t)(G::XS + K * K * 64 * MB);
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t tw = cdiv(d.OW, 16 * NBW), th = cdiv(d.OH, G::WH), td = cdiv(d.OD, G::WD);
+    const int64_t tiles = tw * th * td * d.N * cdiv(d.O, 16 * MB);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), lds, s, x, w, b, y, d, tiles,
+                       (int)tw, (int)th, (int)td);
+    return hipGetLastError();
+}
+
+template <int K, int S, bool ACT>
+hipError_t launch_staged(const float *x, const float *w, const float *b, float *y,
+                         const Conv3dDims &d, hipStream_t s)
+{
+    constexpr int NBW = S == 1 ? 4 : 2;  // output columns per wave: 64 or 32
+    const int sw = conv_store_width(y, d.OW);
+    if (d.O > 16) {
+        if (sw == 4) return launch_staged_sw<4, NBW, K, S, ACT, 4>(x, w, b, y, d, s);
+        if (sw == 2) return launch_staged_sw<4, NBW, K, S, ACT, 2>(x, w, b, y, d, s);
+        return launch_staged_sw<4, NBW, K, S, ACT, 1>(x, w, b, y, d, s);
+    }
+    if (sw == 4) return launch_staged_sw<1, NBW, K, S, ACT, 4>(x, w, b, y, d, s);
+    if (sw == 2) return launch_staged_sw<1, NBW, K, S, ACT, 2>(x, w, b, y, d, s);
+    return launch_staged_sw<1, NBW, K, S, ACT, 1>(x, w, b, y, d, s);
+}
+
 template <bool ACT>
 hipError_t launch_conv3d_generic(const float *x, const float *w, const float *b, float *y,
                                  const Conv3dDims &d, const GenConv &g, hipStream_t s)
 {
+    if (g.stride == 1) {
+        if (g.k == 3) return launch_staged<3, 1, ACT>(x, w, b, y, d, s);
+        if (g.k == 5) return launch_staged<5, 1, ACT>(x, w, b, y, d, s);
+        if (g.k == 7) return launch_staged<7, 1, ACT>(x, w, b, y, d, s);
+    } else if (g.stride == 2) {
+        if (g.k == 3) return launch_staged<3, 2, ACT>(x, w, b, y, d, s);
+        if (g.k == 5) return launch_staged<5, 2, ACT>(x, w, b, y, d, s);
+        if (g.k == 7) return launch_staged<7, 2, ACT>(x, w, b, y, d, s);
+    }
     constexpr int NB = 2;
     const int64_t tw = cdiv(d.OW, 16 * NB);
     unsigned grid;

@@ -1,5 +1,6 @@
 """GPU parity of the general-parameter kernels (any kernel size, stride, padding, dilation,
-pooling window) against the fp64 CPU oracle, through the C ABI.  Same tolerances as the
+pooling window; Conv3d kernel sizes 3/5/7 at strides 1/2 run the LDS-staged kernel, other
+ones the direct kernel) against the fp64 CPU oracle, through the C ABI.  Same tolerances as the
 tuned kernels: |gpu - ref| <= 1e-4 + 1e-4 |ref| elementwise for conv3d_mish_tanh and
 dwsep_conv2d, relative 1e-4 per batch scalar for the pooled sum.  Every case here uses
 parameters outside the tuned kernels' range (k != 3, stride > 1, pad > 2, pool != 2,
@@ -22,6 +23,9 @@ ACT_CASES = [
     (1, 3, 7, 8, 21, 16, 2, 3, 0, True),      # even kernel, stride 3
     (1, 4, 5, 6, 17, 33, 3, 1, 4, True),      # padding wider than the kernel reach
     (1, 2, 12, 12, 12, 5, 7, 2, 3, True),     # k = 7
+    (1, 6, 10, 12, 70, 20, 7, 1, 3, True),    # k = 7 stride 1, two column tiles, ragged W
+    (2, 9, 9, 9, 33, 16, 5, 2, 0, False),     # k = 5 stride 2, one channel block, no padding
+    (1, 5, 4, 5, 9, 7, 3, 1, 3, True),        # k = 3 with padding 3: more padding than input
 ]
 
 
