@@ -418,6 +418,232 @@ __global__ __launch_bounds__(64 * kGenWaves) void dwsep_generic_kernel(
         }
 }
 
+// Accumulators of a pixel-rows MFMA tile start at the pointwise bias: element r of
+// acc[mb][.] is output channel 16*mb + lane%16.
+template <int MB, int R>
+__device__ __forceinline__ void acc_init_pixrows(floatx4 (&acc)[MB][R], const float *bs)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const float v = bs[16 * mb + (lane & 15)];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[mb][r] = floatx4{v, v, v, v};
+    }
+}
+
+// ------------------------------------------------------------------ staged general dwsep
+// Workgroup = 4 waves side by side; tile = R output rows x 64 output columns of image n,
+// output channels [obase, obase + ocnt).  The K loop runs over chunks of 8 input channels,
+// double-buffered in LDS: while a chunk computes, the next chunk's input rows stream from
+// global memory straight into the other LDS buffer (buffer loads with an LDS destination: no
+// registers held, zero padding from dropped offsets) and its weights pass through registers.
+// A chunk holds the HR input rows and the input columns the tile reaches, per channel, the
+// depthwise taps and bias, and the pointwise weights in fragment order.  Staged column c of
+// a row is input column qa + c, qa = the tile's first input column rounded down to a multiple
+// of 4 (so rows of a 4-aligned input can be staged 16 bytes per lane).  Lane l of wave w forms
+// the MFMA operand of k-step cg, the depthwise output of chunk channel 4*cg + l/16 at output
+// column 16*w + l%16 of each row, from K*K LDS reads; the pixels are the MFMA rows, so each
+// lane ends with 4 consecutive pixels of one output channel.
+constexpr int kDwsCC = 8;     // input channels per chunk
+constexpr int kDwsCPL = 5;    // staged column blocks of 64 (staged row <= 320 floats)
+constexpr int kDwsKT = 64;    // depthwise slots per channel (K*K taps + bias, K <= 7)
+
+// Geometry with every size a run-time value (any K <= 7, stride, dilation).
+struct DwStagedGeom {
+    int K, S, dil;   // kernel size, stride, dilation
+    int HR, COLS;    // input rows / columns the tile reaches
+    int RS, CS, XS;  // LDS row stride (COLS + 3 rounded up to 4), channel stride, halo floats
+    int vec, vin;    // output rows 16-byte aligned; input rows 16-byte aligned (W % 4 == 0)
+};
+
+// The same geometry fixed at compile time (kernel size, stride, dilation as template
+// arguments), so that every LDS offset of the depthwise step is an immediate.
+template <int R, int K_, int S_, int D_>
+struct DwFixedGeom {
+    static constexpr int K = K_, S = S_, dil = D_;
+    static constexpr int HR = (R - 1) * S + (K - 1) * dil + 1;
+    static constexpr int COLS = 63 * S + (K - 1) * dil + 1;
+    static constexpr int RS = round_up(COLS + 3, 4);
+    static constexpr int CS = halo_channel_stride(HR * RS);
+    static constexpr int XS = kDwsCC * CS;
+    int vec, vin;
+};
+
+template <int MB>
+constexpr int dws_buffer_floats(int XS)
+{
+    return XS + kDwsCC * 16 * MB + kDwsCC * kDwsKT;
+}
+
+template <int MB, int R, int K, class GEO>
+__global__ __launch_bounds__(256, 2) void dwsep_staged_kernel(
+    const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
+    const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
+    DwsepDims d, GEO g, int64_t tiles, int tiles_w, int tiles_h)
+{
+    // buffer b: halo [8][HR][RS] at channel stride CS, pointwise [2][64][MB] (fragment
+    // order), depthwise [8][64] (taps, bias at K*K); then the pointwise bias [16*MB]
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    constexpr int TAPS = K * K;
+    const int BF = dws_buffer_floats<MB>(g.XS);
+    float *bs = dyn + 2 * BF;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int C = (int)d.C, H = (int)d.H, W = (int)d.W;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w);
+    t /= tiles_w;
+    const int th = (int)(t % tiles_h);
+    t /= tiles_h;
+    const int64_t n = t % d.N;
+    const int obase = (int)(t / d.N) * 16 * MB;
+    const int ocnt = (int)(d.O - obase < 16 * MB ? d.O - obase : 16 * MB);
+    const int h0 = th * R, w0 = tw * 64;
+    const int ih0 = h0 * g.S - d.pad, iw0 = w0 * g.S - d.pad;
+    const int sh = iw0 & 3, qa = iw0 - sh;  // staged column c = input column qa + c
+    const int span = g.COLS + sh;           // staged columns of a row
+    const bool active = w0 + 16 * wave < d.Wo;
+
+    // Per-lane part of the row loads, fixed for the tile: 16-byte quads (lane l: columns
+    // qa + 4l ..) when the input rows are 16-byte aligned, else 4-byte columns l + 64j.
+    const int nq = (span + 3) >> 2;
+    const int qcol = qa + 4 * lane;
+    const bool qok = lane < nq && (unsigned)qcol < (unsigned)W;
+
+    // Issue the input rows of chunk c0 into buffer xsb (row r: channel r / HR, row r % HR).
+    // Byte offsets over the channels [c0, c0 + 8) of image n stay below 2^31 (host check).
+    auto rows_dma = [&](int c0, float *xsb) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(x + (n * C + c0) * (int64_t)H * W);
+        constexpr int CH = kDwsCC;
+        for (int r = wave; r < CH * g.HR; r += 4) {
+            const int cl = r / g.HR, hr = r - cl * g.HR;
+            const int ih = ih0 + hr;
+            const bool rowok = c0 + cl < C && (unsigned)ih < (unsigned)H;
+            const int rowoff = (cl * H + ih) * W;
+            float *dst = xsb + cl * g.CS + hr * g.RS;
+            if (g.vin) {
+                const int off = rowok && qok ? 4 * (rowoff + qcol) : kDropOffset;
+                if (lane < nq)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < kDwsCPL; ++jj) {
+                    if (64 * jj >= span) break;
+                    const int col = 64 * jj + lane, iw = qa + col;
+                    const int off =
+                        rowok && (unsigned)iw < (unsigned)W ? 4 * (rowoff + iw) : kDropOffset;
+                    if (col < span)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rs, (__attribute__((address_space(3))) void *)(dst + 64 * jj), 4, off,
+                            0, 0, 0);
+                }
+            }
+        }
+    };
+    // Weights of chunk c0 in registers: pointwise element (ol, cl) = tid + 256u, depthwise
+    // slot e = tid + 256u of [8][64].
+    float wp[MB / 2], wd[2];
+    auto wload = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < MB / 2; ++u) {
+            const int e = tid + 256 * u, ol = e >> 3, cl = e & 7;
+            wp[u] = (ol < ocnt && c0 + cl < C) ? pw_w[(int64_t)(obase + ol) * C + c0 + cl] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + 256 * u, cl = e >> 6, k = e & 63, c = c0 + cl;
+            float v = 0.0f;
+            if (c < C && k <= TAPS)
+                v = k < TAPS ? dw_w[(int64_t)c * TAPS + k] : (dw_b ? dw_b[c] : 0.0f);
+            wd[u] = v;
+        }
+    };
+    auto wstore = [&](float *buf) {
+        float *ps = buf + g.XS, *dk = ps + kDwsCC * 16 * MB;
+#pragma unroll
+        for (int u = 0; u < MB / 2; ++u) {
+            const int e = tid + 256 * u, ol = e >> 3, cl = e & 7;
+            ps[((cl >> 2) * 64 + (cl & 3) * 16 + (ol & 15)) * MB + (ol >> 4)] = wp[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dk[tid + 256 * u] = wd[u];
+    };
+
+    if (tid < 16 * MB) bs[tid] = (pw_b && tid < ocnt) ? pw_b[obase + tid] : 0.0f;
+    rows_dma(0, dyn);
+    wload(0);
+    wstore(dyn);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    floatx4 acc[MB][R];
+    acc_init_pixrows<MB, R>(acc, bs);
+    const int xoff = sh + (16 * wave + (lane & 15)) * g.S;
+    for (int c0 = 0, b = 0; c0 < C; c0 += kDwsCC, b ^= 1) {
+        float *cur = dyn + b * BF, *nxt = dyn + (b ^ 1) * BF;
+        const bool more = c0 + kDwsCC < C;
+        if (more) {
+            rows_dma(c0 + kDwsCC, nxt);
+            wload(c0 + kDwsCC);
+        }
+        if (active) {
+            const float *ps = cur + g.XS, *dk = ps + kDwsCC * 16 * MB;
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                const int cl = 4 * cg + (lane >> 4);
+                const float *xc = cur + cl * g.CS + xoff;
+                const float *kc = dk + cl * kDwsKT;
+                float pwf[MB];
+                load_afrag<MB>(ps + (cg * 64 + lane) * MB, pwf);
+                float tap[TAPS];
+#pragma unroll
+                for (int k = 0; k < TAPS; ++k) tap[k] = kc[k];
+                const float dbias = kc[TAPS];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float xv[TAPS];
+#pragma unroll
+                    for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+                        for (int kw = 0; kw < K; ++kw)
+                            xv[kh * K + kw] = xc[(r * g.S + kh * g.dil) * g.RS + kw * g.dil];
+                    float v = dbias;
+#pragma unroll
+                    for (int k = 0; k < TAPS; ++k) v = fmaf(tap[k], xv[k], v);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb][r] = mfma_16x16x4(v, pwf[mb], acc[mb][r]);
+                }
+            }
+        }
+        if (more) wstore(nxt);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the next chunk are in LDS
+        lds_barrier();                  // ... and every wave's; nobody reads cur any more
+    }
+    if (!active) return;
+    // lane holds pixels wc .. wc + 3 of output channel obase + 16*mb + lane%16
+    const int wc = w0 + 16 * wave + 4 * (lane >> 4);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int ol = 16 * mb + (lane & 15);
+        if (ol >= ocnt) continue;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int oh = h0 + r;
+            if (oh >= d.Ho) continue;
+            float *yr = y + ((n * d.O + obase + ol) * d.Ho + oh) * d.Wo;
+            if (g.vec && wc + 3 < d.Wo) {
+                *reinterpret_cast<floatx4 *>(yr + wc) = acc[mb][r];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (wc + i < d.Wo) yr[wc + i] = acc[mb][r][i];
+            }
+        }
+    }
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline hipError_t launch_waves(int64_t tiles, unsigned &grid)
@@ -551,10 +777,107 @@ hipError_t launch_conv3d_div_maxpool_generic(const float *x, const float *w,
     return launch_pool_generic<true>(x, w, conv_b, y, p, g, pool, s);
 }
 
+namespace {
+
+template <int MB, int R, int K, class GEO>
+hipError_t launch_dwsep_staged_g(const float *x, const float *dw_w, const float *dw_b,
+                                 const float *pw_w, const float *pw_b, float *y,
+                                 const DwsepDims &d, const GEO &geo, size_t lds, hipStream_t s)
+{
+    auto kern = dwsep_staged_kernel<MB, R, K, GEO>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t tw = cdiv(d.Wo, 64), th = cdiv(d.Ho, R);
+    const int64_t tiles = tw * th * d.N * cdiv(d.O, 16 * MB);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, s, x, dw_w, dw_b, pw_w, pw_b,
+                       y, d, geo, tiles, (int)tw, (int)th);
+    return hipGetLastError();
+}
+
+template <int MB, int R, int K, int S, int D>
+hipError_t launch_dwsep_fixed(const float *x, const float *dw_w, const float *dw_b,
+                              const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
+                              const DwStagedGeom &sg, hipStream_t s)
+{
+    using FG = DwFixedGeom<R, K, S, D>;
+    FG fg;
+    fg.vec = sg.vec;
+    fg.vin = sg.vin;
+    const size_t lds = 4 * (2 * (size_t)dws_buffer_floats<MB>(FG::XS) + 16 * MB);
+    return launch_dwsep_staged_g<MB, R, K, FG>(x, dw_w, dw_b, pw_w, pw_b, y, d, fg, lds, s);
+}
+
+template <int MB, int R>
+hipError_t launch_dwsep_staged(const float *x, const float *dw_w, const float *dw_b,
+                               const float *pw_w, const float *pw_b, float *y,
+                               const DwsepDims &d, const DwStagedGeom &sg, size_t lds,
+                               hipStream_t s)
+{
+    // the pages' kernel sizes 3/5/7 at stride and dilation 1 or 2: compile-time geometry
+#define CONVFUSE_FIXED(KK, SS, DD)                                                               \
+    if (sg.K == KK && sg.S == SS && sg.dil == DD)                                                \
+        return launch_dwsep_fixed<MB, R, KK, SS, DD>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, s);
+    CONVFUSE_FIXED(3, 1, 2) CONVFUSE_FIXED(3, 2, 1) CONVFUSE_FIXED(3, 2, 2)
+    CONVFUSE_FIXED(5, 1, 1) CONVFUSE_FIXED(5, 1, 2) CONVFUSE_FIXED(5, 2, 1) CONVFUSE_FIXED(5, 2, 2)
+    CONVFUSE_FIXED(7, 1, 1) CONVFUSE_FIXED(7, 1, 2) CONVFUSE_FIXED(7, 2, 1) CONVFUSE_FIXED(7, 2, 2)
+#undef CONVFUSE_FIXED
+    switch (sg.K) {
+    case 1: return launch_dwsep_staged_g<MB, R, 1>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    case 2: return launch_dwsep_staged_g<MB, R, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    case 3: return launch_dwsep_staged_g<MB, R, 3>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    case 4: return launch_dwsep_staged_g<MB, R, 4>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    case 5: return launch_dwsep_staged_g<MB, R, 5>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    case 6: return launch_dwsep_staged_g<MB, R, 6>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    default: return launch_dwsep_staged_g<MB, R, 7>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+    }
+}
+
+// The staged kernel's run-time geometry; false when it does not apply (kernel above 7, tile
+// above the LDS size, or the chunk's input bytes beyond 32-bit offsets).  The LDS size is the
+// largest of the run-time and compile-time layouts (they are the same).
+template <int MB, int R>
+bool dwsep_staged_geom(const DwsepDims &d, const GenConv &g, const float *x, const float *y,
+                       DwStagedGeom &sg, size_t &lds)
+{
+    if (g.k < 1 || g.k > 7 || 4 * kDwsCC * d.H * d.W > kBufRange) return false;
+    const int64_t reach = (int64_t)(g.k - 1) * g.dilation;
+    const int64_t HR = (int64_t)(R - 1) * g.stride + reach + 1;
+    const int64_t COLS = 63LL * g.stride + reach + 1;
+    if (COLS + 3 > 64 * kDwsCPL || HR > 4096) return false;
+    sg.K = g.k;
+    sg.S = g.stride;
+    sg.dil = g.dilation;
+    sg.HR = (int)HR;
+    sg.COLS = (int)COLS;
+    sg.RS = round_up((int)COLS + 3, 4);
+    sg.CS = halo_channel_stride(sg.HR * sg.RS);
+    sg.XS = kDwsCC * sg.CS;
+    sg.vec = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
+    // 16-byte row loads: 4-aligned rows and at most 64 quads per staged row
+    sg.vin = d.W % 4 == 0 && ((uintptr_t)x & 15) == 0 && COLS + 3 <= 256;
+    lds = 4 * (2 * (size_t)dws_buffer_floats<MB>(sg.XS) + 16 * MB);
+    return lds <= 160 * 1024;
+}
+
+}  // namespace
+
 hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const float *dw_b,
                                        const float *pw_w, const float *pw_b, float *y,
                                        const DwsepDims &d, const GenConv &g, hipStream_t s)
 {
+    // LDS-staged kernel when it applies (64 or 128 output channels per workgroup)
+    {
+        DwStagedGeom sg;
+        size_t lds;
+        if (d.O > 64) {
+            if (dwsep_staged_geom<8, 2>(d, g, x, y, sg, lds))
+                return launch_dwsep_staged<8, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+        } else if (dwsep_staged_geom<4, 2>(d, g, x, y, sg, lds)) {
+            return launch_dwsep_staged<4, 2>(x, dw_w, dw_b, pw_w, pw_b, y, d, sg, lds, s);
+        }
+    }
     const int64_t tw = cdiv(d.Wo, 16);
     unsigned grid;
     if (d.O > 64) {

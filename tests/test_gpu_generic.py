@@ -70,6 +70,10 @@ DW_CASES = [
     (2, 7, 11, 17, 9, 3, 1, 2, 2, True),       # dilation 2
     (1, 4, 9, 19, 8, 3, 2, 1, 1, False),       # stride 2
     (1, 6, 8, 8, 70, 3, 1, 4, 1, True),        # padding 4
+    (1, 10, 9, 40, 24, 4, 1, 2, 1, True),      # even kernel K = 4
+    (2, 13, 12, 70, 130, 6, 2, 3, 2, False),   # K = 6, stride 2, dilation 2, ragged slices
+    (1, 16, 20, 30, 8, 2, 1, 0, 3, True),      # K = 2, dilation 3, no padding
+    (1, 9, 7, 200, 72, 7, 1, 3, 1, True),      # K = 7, four column tiles
 ]
 
 
