@@ -268,6 +268,169 @@ __global__ __launch_bounds__(64 * kGenWaves) void conv3d_mish_tanh_generic_kerne
         }
 }
 
+// ------------------------------------------------------------------ staged general pool
+// Conv3d (kernel K, stride 1, no padding), divide, P x P x P max-pool, then the pooled
+// channel sum (or, STORE, the pooled tensor), for K in {1, 3, 5} and P in {2, 3, 4}.
+// Workgroup = 4 waves; wave w owns pooled row (n, pd0, ph0 + w), TWP pooled columns from pw0,
+// and output channels [o0, o0 + 16).  Its conv voxels come in NB = P*P*NBW blocks
+// (dd, dh, q): conv voxel (P*pd0 + dd, P*(ph0 + w) + dh, P*pw0 + BW*q + j) for MFMA row j,
+// BW = the largest multiple of P up to 16 (a block's last 16 - BW rows are not used).  The K
+// loop runs over chunks of four input channels at one kernel depth kd, double-buffered in
+// LDS: P depth planes x HHR rows x COLS columns per channel, streamed from global memory
+// straight into LDS, and K*K taps of weights in A-fragment order (through registers).  The
+// epilogue takes each window's extreme over (dd, dh) in registers and over its P columns
+// through wave-private LDS.
+template <int K, int P, int NBW>
+struct PoolGeom {
+    static constexpr int NT = 256;
+    static constexpr int BW = 16 - 16 % P;                   // used columns per block
+    static constexpr int TWP = NBW * BW / P;                 // pooled columns per wave
+    static constexpr int NB = P * P * NBW;                   // voxel blocks per wave
+    static constexpr int HHR = 4 * P + K - 1;                // input rows per (channel, plane)
+    static constexpr int COLS = BW * (NBW - 1) + 16 + K - 1; // input columns per row (<= 64)
+    static constexpr int RS = round_up(COLS, 4);
+    static constexpr int CS = halo_channel_stride(P * HHR * RS);
+    static constexpr int XS = 4 * CS;
+    static constexpr int ROWS = 4 * P * HHR;                 // staged rows per chunk
+    static constexpr int WSZ = K * K * 64;                   // weights per chunk (16 outputs)
+    static constexpr int BUF = XS + WSZ;                     // one stage
+    static constexpr int RED = 16 * (16 * NBW + 1);          // per-wave window buffer
+    static constexpr int LDS = 2 * BUF + 4 * RED;            // floats
+    static_assert(COLS <= 64, "one load per staged row");
+};
+
+template <int K, int P, int NBW, bool STORE>
+__global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
+    float *__restrict__ out, PoolDims p, int64_t tiles, int tiles_w, int tiles_h,
+    float inv_count)
+{
+    using G = PoolGeom<K, P, NBW>;
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float *red = dyn + 2 * G::BUF + wave * G::RED;
+    const Conv3dDims &d = p.conv;
+    const int D = (int)d.D, H = (int)d.H, W = (int)d.W;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w); t /= tiles_w;
+    const int th = (int)(t % tiles_h); t /= tiles_h;
+    const int pd0 = (int)(t % p.PD); t /= p.PD;
+    const int64_t n = t % d.N;
+    const int o0 = (int)(t / d.N) * 16;
+    const int ph0 = th * 4, pw0 = tw * G::TWP;
+    const int xlane = (lane >> 4) * G::CS + wave * P * G::RS + (lane & 15);
+    const int id0 = P * pd0, ih0 = P * ph0, iw0 = P * pw0;
+
+    // Issue chunk q's input rows into buffer xsb: row r = channel r / (P*HHR), plane
+    // (r / HHR) % P, row r % HHR; LDS column c holds input column iw0 + c.  Byte offsets over
+    // the chunk's four channels of image n stay below 2^31 (host check).
+    auto rows_dma = [&](int q, float *xsb) {
+        const int c0 = (q / K) * 4, kd = q % K;
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(x + (n * d.C + c0) * (int64_t)D * H * W);
+        const int iw = iw0 + lane;
+        const bool colok = lane < G::COLS && iw < W;
+        for (int r = wave; r < G::ROWS; r += 4) {
+            const int cl = r / (P * G::HHR), rem = r - cl * (P * G::HHR);
+            const int pl = rem / G::HHR, hr = rem - pl * G::HHR;
+            const int id = id0 + pl + kd, ih = ih0 + hr;
+            const bool ok = colok && c0 + cl < d.C && id < D && ih < H;
+            const int off = ok ? 4 * (((cl * D + id) * H + ih) * W + iw) : kDropOffset;
+            if (lane < G::COLS)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs,
+                    (__attribute__((address_space(3))) void *)(xsb + cl * G::CS +
+                                                               (pl * G::HHR + hr) * G::RS),
+                    4, off, 0, 0, 0);
+        }
+    };
+    WeightChunk<1, 4, G::NT, K * K> wts;
+    auto wload = [&](int q) { wts.load(w, d, o0, (q / K) * 4, K * K * K, (q % K) * K * K); };
+
+    const int chunks = (int)((d.C + 3) / 4) * K;  // chunk q: channels 4*(q/K).., depth q%K
+    rows_dma(0, dyn);
+    wload(0);
+    wts.store(dyn + G::XS);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int ph = ph0 + wave;
+    const bool active = ph < p.PH;
+    floatx4 acc[G::NB];
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < chunks; ++q) {
+        const float *xs = dyn + (q & 1) * G::BUF, *ws = xs + G::XS;
+        float *nxt = dyn + ((q & 1) ^ 1) * G::BUF;
+        const bool more = q + 1 < chunks;
+        if (more) {
+            rows_dma(q + 1, nxt);
+            wload(q + 1);
+        }
+        if (active) {
+#pragma unroll
+            for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+                for (int kw = 0; kw < K; ++kw) {
+                    const float a = ws[(kh * K + kw) * 64 + lane];
+#pragma unroll
+                    for (int dd = 0; dd < P; ++dd)
+#pragma unroll
+                        for (int dh = 0; dh < P; ++dh)
+#pragma unroll
+                            for (int qb = 0; qb < NBW; ++qb) {
+                                const int nb = (dd * P + dh) * NBW + qb;
+                                const float bv = xs[xlane + (dd * G::HHR + dh + kh) * G::RS +
+                                                    G::BW * qb + kw];
+                                acc[nb] = mfma_16x16x4(bv, a, acc[nb]);
+                            }
+                }
+        }
+        if (more) wts.store(nxt + G::XS);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's rows of the next chunk are in LDS
+        __syncthreads();                // ... and every wave's; nobody reads this stage
+    }
+    if (!active) return;  // (no barrier follows)
+    // lane holds columns 4*(lane/16) + r of every block of output channel o0 + lane%16
+    const bool use_min = p.divisor < 0.0f;
+    const int j = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+    for (int qb = 0; qb < NBW; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float m = acc[qb][r];
+#pragma unroll
+            for (int b2 = 1; b2 < P * P; ++b2) {
+                const float v = acc[b2 * NBW + qb][r];
+                m = use_min ? fminf(m, v) : fmaxf(m, v);
+            }
+            red[j * (16 * NBW + 1) + 16 * qb + g4 + r] = m;
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float part = 0.0f;
+    for (int e = lane; e < 16 * G::TWP; e += 64) {
+        const int ol = e / G::TWP, wq = e % G::TWP;
+        const int o = o0 + ol, pw = pw0 + wq;
+        if (o >= d.O || pw >= p.PW) continue;
+        const int col = (wq / (G::BW / P)) * 16 + (wq % (G::BW / P)) * P;  // window's first
+        const float *rp = red + ol * (16 * NBW + 1) + col;
+        float m = rp[0];
+#pragma unroll
+        for (int i = 1; i < P; ++i) m = use_min ? fminf(m, rp[i]) : fmaxf(m, rp[i]);
+        const float v = (m + (cb ? cb[o] : 0.0f)) / p.divisor;
+        if constexpr (STORE)
+            out[(((n * d.O + o) * p.PD + pd0) * p.PH + ph) * p.PW + pw] = v;
+        else
+            part += v;
+    }
+    if constexpr (!STORE) {
+        part = wave_sum(part);
+        if (lane == 0) atomicAdd(out + n, part * inv_count);
+    }
+}
+
 // Pooled channel sum for any window size P (<= 16*NB): a wave owns pooled row (n, pd, ph)
 // and pooled columns [pw0, pw0 + TWP), TWP = floor(16*NB / P), and all output channels of
 // its group.  For each of the P*P conv rows of the window row it computes the conv outputs
@@ -739,12 +902,49 @@ hipError_t launch_conv3d_bias_generic(const float *x, const float *w, const floa
 
 namespace {
 
+template <int K, int P, bool STORE>
+hipError_t launch_pool_staged(const float *x, const float *w, const float *conv_b, float *out,
+                              const PoolDims &p, hipStream_t s)
+{
+    constexpr int NBW = P <= 3 ? 2 : 1;
+    using G = PoolGeom<K, P, NBW>;
+    const Conv3dDims &d = p.conv;
+    const int64_t tw = cdiv(p.PW, G::TWP), th = cdiv(p.PH, 4);
+    const int64_t tiles = tw * th * p.PD * d.N * cdiv(d.O, 16);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    auto kern = conv3d_pool_staged_kernel<K, P, NBW, STORE>;
+    const size_t lds = 4 * (size_t)G::LDS;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), lds, s, x, w, conv_b, out, p,
+                       tiles, (int)tw, (int)th, inv_count);
+    return hipGetLastError();
+}
+
+template <int K, bool STORE>
+hipError_t launch_pool_staged_p(const float *x, const float *w, const float *conv_b, float *out,
+                                const PoolDims &p, int pool, hipStream_t s)
+{
+    if (pool == 2) return launch_pool_staged<K, 2, STORE>(x, w, conv_b, out, p, s);
+    if (pool == 3) return launch_pool_staged<K, 3, STORE>(x, w, conv_b, out, p, s);
+    return launch_pool_staged<K, 4, STORE>(x, w, conv_b, out, p, s);
+}
+
 template <bool STORE>
 hipError_t launch_pool_generic(const float *x, const float *w, const float *conv_b, float *out,
                                const PoolDims &p, const GenConv &g, int pool, hipStream_t s)
 {
-    constexpr int MB = 1, NB = 2;
+    // staged kernel: four input channels of one image within 32-bit byte offsets
     const Conv3dDims &d = p.conv;
+    if (pool >= 2 && pool <= 4 && g.stride == 1 && d.pad == 0 &&
+        16 * d.D * d.H * d.W <= kBufRange) {
+        if (g.k == 1) return launch_pool_staged_p<1, STORE>(x, w, conv_b, out, p, pool, s);
+        if (g.k == 3) return launch_pool_staged_p<3, STORE>(x, w, conv_b, out, p, pool, s);
+        if (g.k == 5) return launch_pool_staged_p<5, STORE>(x, w, conv_b, out, p, pool, s);
+    }
+    constexpr int MB = 1, NB = 2;
     if (pool < 1 || pool > 16 * NB || pool > kGenericMaxPool) return hipErrorInvalidValue;
     const int twp = 16 * NB / pool;
     const int64_t tw = cdiv(p.PW, twp);

@@ -62,6 +62,25 @@ def test_pool_general(case):
     assert rel.max() <= POOL_RTOL, (case, got, ref)
 
 
+MAXPOOL_CASES = [
+    # (N, C, D, H, W, O, k, pool, divisor, conv_bias): the pooled tensor
+    (1, 5, 9, 15, 40, 16, 3, 3, 2.0, True),     # pool 3: windows straddle 16-column blocks
+    (2, 3, 11, 23, 30, 20, 5, 4, -1.5, True),   # k = 5, pool 4, negative divisor, two groups
+    (1, 6, 6, 14, 70, 9, 1, 2, 3.0, False),     # k = 1, pool 2, several column tiles
+    (1, 4, 12, 30, 33, 16, 3, 3, 0.5, True),    # pooled rows past one workgroup's four
+]
+
+
+@pytest.mark.parametrize("case", MAXPOOL_CASES)
+def test_maxpool_tensor_general(case):
+    N, C, D, H, W, O, k, pool, div, cbias = case
+    inp = wl.conv3d_pool_inputs(550 + int(sum(case)), N, C, D, H, W, O, k=k, conv_bias=cbias)
+    ref = oracle.conv3d_div_maxpool(inp["x"], inp["w"], inp["conv_b"], div, pool)
+    y = cf().conv3d_div_maxpool(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]), div, pool)
+    assert tuple(y.shape) == ref.shape
+    assert_close(y.cpu().numpy(), ref, "pooled tensor general %s" % (case,))
+
+
 DW_CASES = [
     # (N, C, H, W, O, K, stride, pad, dilation, bias)
     (2, 8, 13, 30, 16, 1, 1, 0, 1, True),      # pointwise only (K = 1)
