@@ -76,6 +76,27 @@ def work(w):
     return macs, nbytes
 
 
+def kernel_name(w):
+    """The kernel a workload's entry point launches (the launchers' dispatch rules)."""
+    p = w.params
+    if w.op == "conv3d_mish_tanh":
+        if p["k"] == 3 and p["stride"] == 1 and p["pad"] <= 2:
+            return "conv3d_mish_tanh_kernel"
+        if p["k"] in (3, 5, 7) and p["stride"] in (1, 2):
+            return "conv3d_staged_kernel"
+        return "conv3d_mish_tanh_generic_kernel"
+    if w.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
+        if p["k"] == 3 and p["pool"] == 2:
+            return "conv3d_pool_sum_kernel"
+        if p["k"] in (1, 3, 5) and p["pool"] in (2, 3, 4):
+            return "conv3d_pool_staged_kernel"
+        return "conv3d_pool_sum_generic_kernel"
+    tuned = p["K"] == 3 and p["stride"] == 1 and p["dilation"] == 1 and p["pad"] <= 2
+    if w.op == "dwsep_conv2d_split_bf16" and tuned:
+        return "dwsep_split_kernel"
+    return "dwsep_persistent_kernel" if tuned else "dwsep_staged_kernel"
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     csrc = ROOT / "implicit_gemm_convolution_conv3d_amd" / "csrc"
@@ -373,11 +394,7 @@ def main():
     value = 2 * step_macs / (ms_per_step * 1e-3) / 1e12
 
     dmacs, dbytes = work(dominant)
-    kname = {"conv3d_mish_tanh": "conv3d_mish_tanh_kernel",
-             "conv3d_div_maxpool_gap_bias_sum": "conv3d_pool_sum_kernel",
-             "conv3d_div_maxpool": "conv3d_pool_sum_kernel",
-             "dwsep_conv2d": "dwsep_persistent_kernel",
-             "dwsep_conv2d_split_bf16": "dwsep_split_kernel"}[dominant.op]
+    kname = kernel_name(dominant)
     achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
