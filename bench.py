@@ -49,7 +49,7 @@ def out_dims(w):
 def work(w):
     """Algorithmic multiply-adds and bytes (inputs + weights + outputs, each once)."""
     d, p = w.dims, w.params
-    if w.op == "conv3d_mish_tanh":
+    if w.op.startswith("conv3d_mish_tanh"):
         k = p["k"]
         od, oh, ow = out_dims(w)
         outs = d["N"] * d["O"] * od * oh * ow
@@ -79,9 +79,9 @@ def work(w):
 def kernel_name(w):
     """The kernel a workload's entry point launches (the launchers' dispatch rules)."""
     p = w.params
-    if w.op == "conv3d_mish_tanh":
+    if w.op.startswith("conv3d_mish_tanh"):
         if p["k"] == 3 and p["stride"] == 1 and p["pad"] <= 2:
-            return "conv3d_mish_tanh_kernel"
+            return "conv3d_mish_tanh_kernel" if w.op == "conv3d_mish_tanh" else "conv3d_split_kernel"
         if p["k"] in (3, 5, 7) and p["stride"] in (1, 2):
             return "conv3d_staged_kernel"
         return "conv3d_mish_tanh_generic_kernel"
@@ -169,8 +169,9 @@ def summarize_traffic(fetch_csv, write_csv, calib_mib):
 
 def run_op(cf, w, t, out):
     p = w.params
-    if w.op == "conv3d_mish_tanh":
-        cf.conv3d_mish_tanh(t["x"], t["w"], t["b"], p["stride"], p["pad"], out=out)
+    if w.op.startswith("conv3d_mish_tanh"):
+        fn = cf.conv3d_mish_tanh if w.op == "conv3d_mish_tanh" else cf.conv3d_mish_tanh_split_bf16
+        fn(t["x"], t["w"], t["b"], p["stride"], p["pad"], out=out)
     elif w.op == "conv3d_div_maxpool_gap_bias_sum":
         cf.conv3d_div_maxpool_gap_bias_sum(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"],
                                            t["bias"], out=out)
@@ -184,7 +185,7 @@ def run_op(cf, w, t, out):
 
 def out_shape(w):
     d = w.dims
-    if w.op == "conv3d_mish_tanh":
+    if w.op.startswith("conv3d_mish_tanh"):
         return (d["N"], d["O"]) + out_dims(w)
     if w.op == "conv3d_div_maxpool_gap_bias_sum":
         return (d["N"],)

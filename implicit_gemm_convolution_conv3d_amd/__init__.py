@@ -17,7 +17,7 @@ from . import _build
 __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
-    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv_out_len",
+    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16", "conv_out_len",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -28,7 +28,7 @@ _ERR_NAMES = {ERR_NULL: "NULL", ERR_SHAPE: "SHAPE", ERR_UNSUPPORTED: "UNSUPPORTE
 EXPORTED_SYMBOLS = (
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
-    "pointwise_conv2d", "dwsep_conv2d_split_bf16",
+    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
 )
 
@@ -63,6 +63,7 @@ def lib():
                 [_vp] * 3 + [ctypes.c_float, _i64, _vp] + [_i64] * 7 + [_vp])
             L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
             L.dwsep_conv2d_split_bf16.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
+            L.conv3d_mish_tanh_split_bf16.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.conv3d_bias.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.mish_tanh.argtypes = [_vp, _vp, _i64, _vp]
             L.div_maxpool_gap_bias_sum.argtypes = (
@@ -112,7 +113,12 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None):
+def conv3d_mish_tanh_split_bf16(x, w, b=None, stride=1, padding=0, out=None):
+    """conv3d_mish_tanh with the implicit GEMM as a three-term bf16 split of fp32 (opt-in)."""
+    return conv3d_mish_tanh(x, w, b, stride, padding, out, _entry="conv3d_mish_tanh_split_bf16")
+
+
+def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None, _entry="conv3d_mish_tanh"):
     """y = tanh(mish(conv3d(x, w) + b)); x [N,Cin,D,H,W], w [Cout,Cin,k,k,k], b [Cout]."""
     import torch
     N, C, D, H, W = x.shape
@@ -125,7 +131,7 @@ def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None):
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
-        _check(lib().conv3d_mish_tanh(_ptr(x, "x"), _ptr(w, "w"), _ptr(b, "b"),
+        _check(getattr(lib(), _entry)(_ptr(x, "x"), _ptr(w, "w"), _ptr(b, "b"),
                                       _ptr(out, "out", shp), N, C, D, H, W, O, k, stride,
                                       padding, _stream(x)))
     return out

@@ -92,38 +92,61 @@ int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, in
     return CONVFUSE_OK;
 }
 
-int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y, int64_t N,
-                     int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout, int64_t k,
-                     int64_t stride, int64_t pad, void *stream)
+// Validation and dispatch shared by conv3d_mish_tanh and its split-bf16 mode.
+static int conv3d_act_entry(const char *fn, bool split, const float *x, const float *w,
+                            const float *b, float *y, int64_t N, int64_t Cin, int64_t D,
+                            int64_t H, int64_t W, int64_t Cout, int64_t k, int64_t stride,
+                            int64_t pad, void *stream)
 {
     if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
-        return fail(CONVFUSE_ERR_SHAPE, "conv3d_mish_tanh: bad N=%lld Cin=%lld Cout=%lld",
-                    (long long)N, (long long)Cin, (long long)Cout);
+        return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
+                    (long long)Cin, (long long)Cout);
     int64_t OD, OH, OW;
     if (!out_len(D, k, stride, pad, 1, &OD) || !out_len(H, k, stride, pad, 1, &OH) ||
         !out_len(W, k, stride, pad, 1, &OW) || OD <= 0 || OH <= 0 || OW <= 0)
         return fail(CONVFUSE_ERR_SHAPE,
-                    "conv3d_mish_tanh: D=%lld H=%lld W=%lld k=%lld stride=%lld pad=%lld give no "
-                    "output",
+                    "%s: D=%lld H=%lld W=%lld k=%lld stride=%lld pad=%lld give no output", fn,
                     (long long)D, (long long)H, (long long)W, (long long)k, (long long)stride,
                     (long long)pad);
     if (!elems_ok({N, Cin, D, H, W}) || !elems_ok({N, Cout, OD, OH, OW}) ||
         !elems_ok({Cout, Cin, k, k, k}))
-        return fail(CONVFUSE_ERR_SHAPE, "conv3d_mish_tanh: tensor too large");
+        return fail(CONVFUSE_ERR_SHAPE, "%s: tensor too large", fn);
     if (!taps_ok(k, 3))
-        return fail(CONVFUSE_ERR_UNSUPPORTED, "conv3d_mish_tanh: k=%lld: more than 2^30 taps",
-                    (long long)k);
+        return fail(CONVFUSE_ERR_UNSUPPORTED, "%s: k=%lld: more than 2^30 taps", fn, (long long)k);
     if (N == 0) return CONVFUSE_OK;
-    if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "conv3d_mish_tanh: x, w and y are required");
+    if (!x || !w || !y) return fail(CONVFUSE_ERR_NULL, "%s: x, w and y are required", fn);
     convfuse::Conv3dDims d{N, Cin, D, H, W, Cout, OD, OH, OW, (int)pad};
-    if (k == 3 && stride == 1 && pad <= 2)
+    if (k == 3 && stride == 1 && pad <= 2) {
+        if (split)
+            return device_status(convfuse::launch_conv3d_mish_tanh_split_bf16(
+                                     x, w, b, y, d, (hipStream_t)stream),
+                                 "conv3d_mish_tanh_split_bf16 launch");
         return device_status(
             convfuse::launch_conv3d_mish_tanh(x, w, b, y, d, (hipStream_t)stream),
             "conv3d_mish_tanh launch");
+    }
+    // other geometries run the fp32 kernels (more accurate than the split contract)
     const convfuse::GenConv g{(int)k, (int)stride, 1};
     return device_status(
         convfuse::launch_conv3d_mish_tanh_generic(x, w, b, y, d, g, (hipStream_t)stream),
-        "conv3d_mish_tanh launch");
+        split ? "conv3d_mish_tanh_split_bf16 launch" : "conv3d_mish_tanh launch");
+}
+
+int conv3d_mish_tanh(const float *x, const float *w, const float *b, float *y, int64_t N,
+                     int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout, int64_t k,
+                     int64_t stride, int64_t pad, void *stream)
+{
+    return conv3d_act_entry("conv3d_mish_tanh", false, x, w, b, y, N, Cin, D, H, W, Cout, k,
+                            stride, pad, stream);
+}
+
+int conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b, float *y,
+                                int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                int64_t Cout, int64_t k, int64_t stride, int64_t pad,
+                                void *stream)
+{
+    return conv3d_act_entry("conv3d_mish_tanh_split_bf16", true, x, w, b, y, N, Cin, D, H, W,
+                            Cout, k, stride, pad, stream);
 }
 
 int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,

@@ -20,6 +20,28 @@ __device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// D(16x16) += A(16x32) * B(32x16) on the bf16 matrix cores, fp32 accumulation.  Lane l
+// supplies A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16] in element i; it receives
+// D[4*(l/16)+r][l%16] in element r of the result (the fp32 16x16x4 layout).
+__device__ __forceinline__ floatx4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Three-term split of fp32 values for bf16 matrix cores: hi = bf16(v) (nearest), lo =
+// bf16(v - hi); v*w is then taken as hi_v*hi_w + hi_v*lo_w + lo_v*hi_w.
+__device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)v[i];
+        hi[i] = h;
+        lo[i] = (__bf16)(v[i] - (float)h);
+    }
+}
+
 // Workgroups are dispatched round-robin over the XCDs (workgroup i lands on XCD i % 8).
 // Remap the linear workgroup id so that each XCD processes one contiguous run of tiles:
 // neighbouring tiles then share their halo rows in the same L2.  Bijective on [0, total).

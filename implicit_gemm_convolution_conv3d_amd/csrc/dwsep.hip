@@ -504,23 +504,6 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
 // the channels g + 4i (i = 0..7) of its pixel (A) or output channel (B), so the four groups
 // read four different LDS bank groups of the halo.  Same tiles, staging, prefetch and
 // epilogue as the persistent fp32 kernel.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ floatx4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void split_bf16(const float (&v)[8], bf16x8 &hi, bf16x8 &lo)
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)v[i];
-        hi[i] = h;
-        lo[i] = (__bf16)(v[i] - (float)h);
-    }
-}
-
 // LDS bytes of the split kernel's weights: pointwise hi and lo fragments (KS k-steps of 32
 // channels x 64 lanes x MB, 16 bytes each), depthwise taps [32*KS][12], pointwise bias.
 template <int MB>

@@ -63,6 +63,10 @@ hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const floa
 
 // dwsep with the pointwise GEMM on bf16 matrix cores as a three-term split of each fp32
 // operand (opt-in precision mode; k = 3, stride 1, dilation 1, pad <= 2).
+// Split-bf16 mode of conv3d_mish_tanh (k = 3, stride 1, pad <= 2).
+hipError_t launch_conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b,
+                                              float *y, const Conv3dDims &d, hipStream_t stream);
+
 hipError_t launch_dwsep_conv2d_split_bf16(const float *x, const float *dw_w, const float *dw_b,
                                           const float *pw_w, const float *pw_b, float *y,
                                           const DwsepDims &d, hipStream_t stream);

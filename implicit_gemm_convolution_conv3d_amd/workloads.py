@@ -86,7 +86,7 @@ class Workload:
     def inputs(self, seed=None):
         s = self.seed if seed is None else seed
         d = self.dims
-        if self.op == "conv3d_mish_tanh":
+        if self.op in ("conv3d_mish_tanh", "conv3d_mish_tanh_split_bf16"):
             return conv3d_act_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                      self.params["k"], bias=True)
         if self.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
@@ -131,4 +131,6 @@ WORKLOADS = {
     11: Workload(11, "dwsep_conv2d_333x517_bias_split_bf16", "dwsep_conv2d_split_bf16",
                  dict(N=8, C=96, H=333, W=517, O=192),
                  dict(K=3, stride=1, pad=1, dilation=1, bias=True)),
+    12: Workload(12, "conv3d_mish_tanh_split_bf16", "conv3d_mish_tanh_split_bf16",
+                 dict(N=16, C=32, D=32, H=64, W=64, O=64), dict(k=3, stride=1, pad=0)),
 }

@@ -126,6 +126,22 @@ int dwsep_conv2d(const float *x, const float *dw_w, const float *dw_b, const flo
                  void *stream);
 
 /*
+ * conv3d_mish_tanh with the implicit GEMM on bf16 matrix cores (opt-in precision mode, the
+ * same three-term split of fp32 as dwsep_conv2d_split_bf16 below: v*w taken as
+ * hi*hi + hi*lo + lo*hi with fp32 accumulation; bias and tanh(mish) in fp32).
+ * Error contract (a separate one from the fp32 entry points): each product is off by at
+ * most 3 * 2^-16 |x*w|, and tanh(mish(.)) changes by at most 1.1 times a change of its
+ * argument, so
+ *     |y - y_exact| <= 1e-4 + 1e-4 |y_exact| + 2^-13 * sum over taps and channels |x * w|.
+ * Same arguments, layouts and errors as conv3d_mish_tanh.  Applies to k = 3, stride 1,
+ * pad <= 2; every other case runs the fp32 kernels (which meet the tighter fp32 contract).
+ */
+int conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b, float *y,
+                                int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                int64_t Cout, int64_t k, int64_t stride, int64_t pad,
+                                void *stream);
+
+/*
  * dwsep_conv2d with the pointwise GEMM on bf16 matrix cores (opt-in precision mode).  The
  * pages weigh reduced-precision tensor-core formats (TF32) against true fp32 for these layers
  * (page "Kimi-K2.6 l2_p47", the roofline estimate and the mma-precision paragraph); gfx950 has

@@ -125,6 +125,22 @@ def test_dwsep_validation(kw, code):
     assert cf.lib().convfuse_last_error().decode().startswith("dwsep_conv2d")
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(w=None), cf.ERR_NULL), (dict(y=None), cf.ERR_NULL),
+    (dict(C=0), cf.ERR_SHAPE), (dict(O=0), cf.ERR_SHAPE), (dict(N=-1), cf.ERR_SHAPE),
+    (dict(D=2), cf.ERR_SHAPE), (dict(p=-1), cf.ERR_SHAPE), (dict(s=0), cf.ERR_SHAPE),
+    (dict(k=1100, D=1 << 12, H=1 << 12, W=1 << 12, C=1, O=1), cf.ERR_UNSUPPORTED),
+])
+def test_conv3d_split_validation(kw, code):
+    args = dict(x=FAKE, w=FAKE, b=None, y=FAKE, N=1, C=4, D=8, H=8, W=8, O=8, k=3, s=1, p=0)
+    args.update(kw)
+    a = args
+    assert cf.lib().conv3d_mish_tanh_split_bf16(a["x"], a["w"], a["b"], a["y"], a["N"], a["C"],
+                                                a["D"], a["H"], a["W"], a["O"], a["k"], a["s"],
+                                                a["p"], None) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("conv3d_mish_tanh_split_bf16")
+
+
 def call_dw_split(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W=8, O=8,
                   K=3, s=1, p=1, d=1):
     return cf.lib().dwsep_conv2d_split_bf16(x, dw, db, pw, pb, y, N, C, H, W, O, K, s, p, d, None)

@@ -1,14 +1,17 @@
-"""GPU parity of dwsep_conv2d_split_bf16, the opt-in mode that runs the pointwise GEMM as a
-three-term bf16 split of fp32 on the matrix cores, against the fp64 CPU oracle through the
-C ABI.
-
-Its error contract is its own: with d[c] the exact depthwise output at the pixel,
+"""GPU parity of the split-bf16 modes (dwsep_conv2d_split_bf16: the pointwise GEMM;
+conv3d_mish_tanh_split_bf16: the Conv3d implicit GEMM) -- opt-in modes that run the
+contraction as a three-term bf16 split of fp32 on the matrix cores -- against the fp64 CPU
+oracle through the C ABI.  The Conv3d mode's contract is
+    |y - y_exact| <= 1e-4 + 1e-4 |y_exact| + 2^-13 * sum over taps and channels |x * w|
+(3 * 2^-16 per product, times tanh(mish)'s slope of at most 1.1), with the sum taken from the
+oracle's Conv3d of |x| and |w|.  The dwsep mode's contract, with d[c] the exact depthwise
+output at the pixel, is
     |y[o] - y_exact[o]| <= 1e-4 + 1e-4 |y_exact[o]| + 2^-14 * sum_c |d[c] * pw[o,c]|
 (bf16 rounding to nearest leaves |v - hi - lo| <= 2^-16 |v| and |lo| <= 2^-8 |v|, so each
 product loses at most 3 * 2^-16 |v*w|).  The sum is computed here from the oracle's depthwise
 output (the oracle's depthwise-separable conv with an identity pointwise step).  Cases cover
-ragged tiles, channel counts off the 32-channel k-step, several output-channel slices, every
-padding the split kernel takes, the full-size workloads on sampled outputs, and a closed form
+ragged tiles, channel counts off the k-steps and chunks, several output-channel slices, every
+padding the split kernels take, the full-size workloads on sampled outputs, and a closed form
 that fixes which of the split's product terms are present."""
 import numpy as np
 import pytest
@@ -146,3 +149,64 @@ def test_split_not_written_past_end():
     cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
                                  dev(inp["pw_w"]), dev(inp["pw_b"]), 1, 1, 1, out=y)
     assert bool((buf[n_out:] == 12345.0).all())
+
+
+CONV_SPLIT_CASES = [
+    # (N, C, D, H, W, O, pad, bias)
+    (1, 8, 6, 9, 20, 16, 0, True),      # one chunk, one channel group
+    (2, 5, 7, 9, 37, 19, 0, True),      # C below the 8-channel chunk, ragged columns
+    (1, 13, 5, 6, 70, 40, 1, False),    # two chunks (ragged), two channel groups, pad 1
+    (1, 32, 6, 7, 64, 64, 2, True),     # the layer's channel shape, pad 2
+    (2, 3, 4, 4, 4, 7, 2, True),        # output larger than input
+]
+
+
+def conv_abs_sum(inp, pad):
+    return oracle.conv3d(np.abs(inp["x"]), np.abs(inp["w"]), None, 1, pad)
+
+
+@pytest.mark.parametrize("case", CONV_SPLIT_CASES)
+def test_conv3d_split_small(case):
+    N, C, D, H, W, O, pad, bias = case
+    inp = wl.conv3d_act_inputs(720 + sum(case), N, C, D, H, W, O, bias=bias)
+    ref = oracle.conv3d_mish_tanh(inp["x"], inp["w"], inp["b"], 1, pad)
+    bound_extra = (2.0 ** -13 / SPLIT_SLACK) * conv_abs_sum(inp, pad)
+    y = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), 1, pad)
+    assert tuple(y.shape) == ref.shape
+    assert_split_close(y.cpu().numpy(), ref, bound_extra, "conv3d split %s" % (case,))
+
+
+def test_conv3d_split_general_parameters_run_fp32():
+    inp = wl.conv3d_act_inputs(790, 1, 4, 9, 10, 21, 8, k=5)
+    ref = oracle.conv3d_mish_tanh(inp["x"], inp["w"], inp["b"], 2, 2)
+    y = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), 2, 2)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-4 + 1e-4 * np.abs(ref))
+
+
+def test_conv3d_split_full_workload_sampled():
+    w = wl.WORKLOADS[12]
+    inp = w.inputs()
+    p = w.params
+    y = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
+                                         p["stride"], p["pad"])
+    assert tuple(y.shape) == (16, 64, 30, 62, 62)
+    idx = edge_indices(y.shape, np.random.default_rng(41), 6000)
+    ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
+    # sum |x * w| at the sampled outputs: the oracle's Conv3d of |x| and |w| over the images
+    # the samples touch
+    n_idx = np.unravel_index(idx, y.shape)[0]
+    extra = np.empty(idx.size)
+    for n in np.unique(n_idx):
+        sel = n_idx == n
+        full = oracle.conv3d(np.abs(inp["x"][n:n + 1]), np.abs(inp["w"]), None, 1, 0)
+        extra[sel] = full.reshape(-1)[idx[sel] - n * full.size]
+    assert_split_close(gather(y, idx), ref, (2.0 ** -13 / SPLIT_SLACK) * extra,
+                       "conv3d split workload sampled")
+    torch = _torch()
+    assert bool(torch.isfinite(y).all())
+    y32 = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), p["stride"], p["pad"])
+    assert not bool(torch.equal(y, y32))
+    y2 = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
+                                          p["stride"], p["pad"])
+    assert bool(torch.equal(y, y2))
