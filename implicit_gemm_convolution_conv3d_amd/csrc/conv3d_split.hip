@@ -24,22 +24,23 @@ namespace {
 constexpr int kSpCC = 8;     // input channels per chunk: the 8 elements of a fragment
 constexpr int kSpSteps = 7;  // k-steps per chunk: 28 taps (27 + one with zero weights)
 
+template <int WD_, int WH_>
 struct SpGeom {
-    static constexpr int WD = 2, WH = 2, NT = 256, NBW = 4;
+    static constexpr int WD = WD_, WH = WH_, NT = 64 * WD * WH, NBW = 4;
     static constexpr int HD = WD + 2, HH = WH + 2, RSX = 72;  // halo column c: ow0 - 4 + c
     static constexpr int POS = HD * HH * RSX;                // halo positions
     static constexpr int PPT = (POS + NT - 1) / NT;          // positions per thread
 };
 
 // One chunk in registers between the global loads and the split LDS stores.
-// x: position p = tid + 256u, 8 channels each.  w: (output, input channel) pair
-// q = tid + 256u, numbered q = (m*MB + mb)*8 + i for output channel o0 + 16*mb + m and input
+// x: position p = tid + NT*u, 8 channels each.  w: (output, input channel) pair
+// q = tid + NT*u, numbered q = (m*MB + mb)*8 + i for output channel o0 + 16*mb + m and input
 // channel c0 + i; its 27 taps are contiguous in memory.
-template <int MB>
+template <int MB, class G>
 struct SpStage {
     static constexpr int PAIRS = 16 * MB * kSpCC;
-    static constexpr int PPQ = (PAIRS + 255) / 256;
-    float xv[SpGeom::PPT][8];
+    static constexpr int PPQ = (PAIRS + G::NT - 1) / G::NT;
+    float xv[G::PPT][8];
     float wv[PPQ][27];
 
     __device__ __forceinline__ void load(const float *__restrict__ x, const float *__restrict__ w,
@@ -49,12 +50,12 @@ struct SpStage {
         const int tid = threadIdx.x;
         const int64_t plane = d.D * d.H * d.W;
 #pragma unroll
-        for (int u = 0; u < SpGeom::PPT; ++u) {
-            const int p = tid + 256 * u;
-            const int hd = p / (SpGeom::HH * SpGeom::RSX), rem = p % (SpGeom::HH * SpGeom::RSX);
-            const int hh = rem / SpGeom::RSX, col = rem % SpGeom::RSX;
+        for (int u = 0; u < G::PPT; ++u) {
+            const int p = tid + G::NT * u;
+            const int hd = p / (G::HH * G::RSX), rem = p % (G::HH * G::RSX);
+            const int hh = rem / G::RSX, col = rem % G::RSX;
             const int id = id0 + hd, ih = ih0 + hh, iw = iw0 + col;
-            const bool ok = p < SpGeom::POS && (unsigned)id < (unsigned)d.D &&
+            const bool ok = p < G::POS && (unsigned)id < (unsigned)d.D &&
                             (unsigned)ih < (unsigned)d.H && (unsigned)iw < (unsigned)d.W;
             const float *src =
                 x + (n * d.C + c0) * plane + ok * (((int64_t)id * d.H + ih) * d.W + iw);
@@ -64,7 +65,7 @@ struct SpStage {
         }
 #pragma unroll
         for (int u = 0; u < PPQ; ++u) {
-            const int q = tid + 256 * u;
+            const int q = tid + G::NT * u;
             const int i = q & 7, mb = (q >> 3) % MB, m = (q >> 3) / MB;
             const int o = o0 + 16 * mb + m, c = c0 + i;
             const bool ok = q < PAIRS && o < d.O && c < d.C;
@@ -81,9 +82,9 @@ struct SpStage {
     {
         const int tid = threadIdx.x;
 #pragma unroll
-        for (int u = 0; u < SpGeom::PPT; ++u) {
-            const int p = tid + 256 * u;
-            if (p >= SpGeom::POS) continue;
+        for (int u = 0; u < G::PPT; ++u) {
+            const int p = tid + G::NT * u;
+            if (p >= G::POS) continue;
             bf16x8 hi, lo;
             split_bf16(xv[u], hi, lo);
             xs_hi[p] = hi;
@@ -91,7 +92,7 @@ struct SpStage {
         }
 #pragma unroll
         for (int u = 0; u < PPQ; ++u) {
-            const int q = tid + 256 * u;
+            const int q = tid + G::NT * u;
             if (q >= PAIRS) continue;
             const int i = q & 7, mb = (q >> 3) % MB, m = (q >> 3) / MB;
 #pragma unroll
@@ -106,12 +107,12 @@ struct SpStage {
     }
 };
 
-template <int MB, bool ACT, int SW>
-__global__ __launch_bounds__(256, 2) void conv3d_split_kernel(
+template <int MB, int WD, int WH, bool ACT, int SW>
+__global__ __launch_bounds__(64 * WD * WH, 8 / (WD * WH)) void conv3d_split_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ b,
     float *__restrict__ y, Conv3dDims d, int64_t tiles, int tiles_w, int tiles_h, int tiles_d)
 {
-    using G = SpGeom;
+    using G = SpGeom<WD, WH>;
     constexpr int NBW = G::NBW;
     constexpr int WENT = kSpSteps * 64 * MB;  // weight fragments per chunk
     __shared__ bf16x8 xs_hi[G::POS], xs_lo[G::POS];
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void conv3d_split_kernel(
         toff[s] = ((wd + kd) * G::HH + wh + kh) * G::RSX + (lane & 15) + kw + 4 - d.pad;
     }
 
-    SpStage<MB> stage;
+    SpStage<MB, G> stage;
     const int id0 = od0 - d.pad, ih0 = oh0 - d.pad, iw0 = ow0 - 4;
     stage.load(x, w, d, n, 0, o0, id0, ih0, iw0);
     const int od = od0 + wd, oh = oh0 + wh;
@@ -186,11 +187,11 @@ __global__ __launch_bounds__(256, 2) void conv3d_split_kernel(
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <int MB, bool ACT>
+template <int MB, int WD, int WH, bool ACT>
 hipError_t launch_split(const float *x, const float *w, const float *b, float *y,
                         const Conv3dDims &d, hipStream_t s)
 {
-    using G = SpGeom;
+    using G = SpGeom<WD, WH>;
     const int64_t tw = cdiv(d.OW, 64), th = cdiv(d.OH, G::WH), td = cdiv(d.OD, G::WD);
     const int64_t tiles = tw * th * td * d.N * cdiv(d.O, 16 * MB);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -199,9 +200,9 @@ hipError_t launch_split(const float *x, const float *w, const float *b, float *y
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), 0, s, x, w, b, y, d, tiles,
                            (int)tw, (int)th, (int)td);
     };
-    if (sw == 4) go(conv3d_split_kernel<MB, ACT, 4>);
-    else if (sw == 2) go(conv3d_split_kernel<MB, ACT, 2>);
-    else go(conv3d_split_kernel<MB, ACT, 1>);
+    if (sw == 4) go(conv3d_split_kernel<MB, WD, WH, ACT, 4>);
+    else if (sw == 2) go(conv3d_split_kernel<MB, WD, WH, ACT, 2>);
+    else go(conv3d_split_kernel<MB, WD, WH, ACT, 1>);
     return hipGetLastError();
 }
 
@@ -210,8 +211,8 @@ hipError_t launch_split(const float *x, const float *w, const float *b, float *y
 hipError_t launch_conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b,
                                               float *y, const Conv3dDims &d, hipStream_t s)
 {
-    if (d.O > 16) return launch_split<2, true>(x, w, b, y, d, s);
-    return launch_split<1, true>(x, w, b, y, d, s);
+    if (d.O > 16) return launch_split<2, 2, 2, true>(x, w, b, y, d, s);
+    return launch_split<1, 2, 2, true>(x, w, b, y, d, s);
 }
 
 }  // namespace convfuse
