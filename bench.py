@@ -56,7 +56,7 @@ def work(w):
         macs = outs * d["C"] * k ** 3
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
                       + d["O"] + outs)
-    elif w.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
+    elif w.op.startswith("conv3d_div_maxpool"):
         k = p["k"]
         od, oh, ow = out_dims(w)
         macs = d["N"] * d["O"] * od * oh * ow * d["C"] * k ** 3
@@ -85,9 +85,10 @@ def kernel_name(w):
         if p["k"] in (3, 5, 7) and p["stride"] in (1, 2):
             return "conv3d_staged_kernel"
         return "conv3d_mish_tanh_generic_kernel"
-    if w.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
+    if w.op.startswith("conv3d_div_maxpool"):
         if p["k"] == 3 and p["pool"] == 2:
-            return "conv3d_pool_sum_kernel"
+            return ("conv3d_pool_split_kernel" if w.op.endswith("split_bf16")
+                    else "conv3d_pool_sum_kernel")
         if p["k"] in (1, 3, 5) and p["pool"] in (2, 3, 4):
             return "conv3d_pool_staged_kernel"
         return "conv3d_pool_sum_generic_kernel"
@@ -172,9 +173,10 @@ def run_op(cf, w, t, out):
     if w.op.startswith("conv3d_mish_tanh"):
         fn = cf.conv3d_mish_tanh if w.op == "conv3d_mish_tanh" else cf.conv3d_mish_tanh_split_bf16
         fn(t["x"], t["w"], t["b"], p["stride"], p["pad"], out=out)
-    elif w.op == "conv3d_div_maxpool_gap_bias_sum":
-        cf.conv3d_div_maxpool_gap_bias_sum(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"],
-                                           t["bias"], out=out)
+    elif w.op.startswith("conv3d_div_maxpool_gap_bias_sum"):
+        fn = (cf.conv3d_div_maxpool_gap_bias_sum if w.op == "conv3d_div_maxpool_gap_bias_sum"
+              else cf.conv3d_div_maxpool_gap_bias_sum_split_bf16)
+        fn(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"], t["bias"], out=out)
     elif w.op == "conv3d_div_maxpool":
         cf.conv3d_div_maxpool(t["x"], t["w"], t["conv_b"], p["divisor"], p["pool"], out=out)
     else:
@@ -187,7 +189,7 @@ def out_shape(w):
     d = w.dims
     if w.op.startswith("conv3d_mish_tanh"):
         return (d["N"], d["O"]) + out_dims(w)
-    if w.op == "conv3d_div_maxpool_gap_bias_sum":
+    if w.op.startswith("conv3d_div_maxpool_gap_bias_sum"):
         return (d["N"],)
     if w.op == "conv3d_div_maxpool":
         pool = w.params["pool"]

@@ -17,7 +17,8 @@ from . import _build
 __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
-    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16", "conv_out_len",
+    "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
+    "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
+    "conv3d_div_maxpool_gap_bias_sum_split_bf16",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
 )
 
@@ -64,6 +66,8 @@ def lib():
             L.dwsep_conv2d.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
             L.dwsep_conv2d_split_bf16.argtypes = [_vp] * 6 + [_i64] * 9 + [_vp]
             L.conv3d_mish_tanh_split_bf16.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
+            L.conv3d_div_maxpool_gap_bias_sum_split_bf16.argtypes = (
+                [_vp] * 3 + [ctypes.c_float, _i64, _vp, _vp] + [_i64] * 7 + [_vp])
             L.conv3d_bias.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.mish_tanh.argtypes = [_vp, _vp, _i64, _vp]
             L.div_maxpool_gap_bias_sum.argtypes = (
@@ -137,7 +141,14 @@ def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None, _entry="conv3d
     return out
 
 
-def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out=None):
+def conv3d_div_maxpool_gap_bias_sum_split_bf16(x, w, conv_b, divisor, pool, bias, out=None):
+    """conv3d_div_maxpool_gap_bias_sum with the Conv3d as a three-term bf16 split (opt-in)."""
+    return conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out,
+                                           _entry="conv3d_div_maxpool_gap_bias_sum_split_bf16")
+
+
+def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out=None,
+                                    _entry="conv3d_div_maxpool_gap_bias_sum"):
     """out[n] = sum_c(mean(maxpool((conv3d(x,w)+conv_b)/divisor)) + bias[c]); out [N]."""
     import torch
     N, C, D, H, W = x.shape
@@ -151,7 +162,7 @@ def conv3d_div_maxpool_gap_bias_sum(x, w, conv_b, divisor, pool, bias, out=None)
     if out is None:
         out = torch.empty((N,), dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
-        _check(lib().conv3d_div_maxpool_gap_bias_sum(
+        _check(getattr(lib(), _entry)(
             _ptr(x, "x"), _ptr(w, "w"), _ptr(conv_b, "conv_b"), float(divisor), pool,
             _ptr(bias, "bias"), _ptr(out, "out", (N,)), N, C, D, H, W, O, k, _stream(x)))
     return out

@@ -149,12 +149,12 @@ int conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b, 
                             Cout, k, stride, pad, stream);
 }
 
-int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
-                                    float divisor, int64_t pool, const float *bias, float *out,
-                                    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
-                                    int64_t Cout, int64_t k, void *stream)
+// Validation and dispatch shared by conv3d_div_maxpool_gap_bias_sum and its split-bf16 mode.
+static int pool_sum_entry(const char *fn, bool split, const float *x, const float *w,
+                          const float *conv_b, float divisor, int64_t pool, const float *bias,
+                          float *out, int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                          int64_t Cout, int64_t k, void *stream)
 {
-    const char *fn = "conv3d_div_maxpool_gap_bias_sum";
     if (N < 0 || N > kMaxDim || Cin <= 0 || Cin > kMaxDim || Cout <= 0 || Cout > kMaxDim)
         return fail(CONVFUSE_ERR_SHAPE, "%s: bad N=%lld Cin=%lld Cout=%lld", fn, (long long)N,
                     (long long)Cin, (long long)Cout);
@@ -182,14 +182,41 @@ int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float 
     if (!x || !w || !bias || !out)
         return fail(CONVFUSE_ERR_NULL, "%s: x, w, bias and out are required", fn);
     convfuse::PoolDims p{{N, Cin, D, H, W, Cout, OD, OH, OW, 0}, PD, PH, PW, divisor};
-    if (k == 3 && pool == 2)
+    const char *what = split ? "conv3d_div_maxpool_gap_bias_sum_split_bf16 launch"
+                             : "conv3d_div_maxpool_gap_bias_sum launch";
+    if (k == 3 && pool == 2) {
+        if (split)
+            return device_status(convfuse::launch_conv3d_pool_sum_split_bf16(
+                                     x, w, conv_b, bias, out, p, (hipStream_t)stream),
+                                 what);
         return device_status(
             convfuse::launch_conv3d_pool_sum(x, w, conv_b, bias, out, p, (hipStream_t)stream),
-            "conv3d_div_maxpool_gap_bias_sum launch");
+            what);
+    }
+    // other parameters run the fp32 kernels (more accurate than the split contract)
     const convfuse::GenConv g{(int)k, 1, 1};
     return device_status(convfuse::launch_conv3d_pool_sum_generic(x, w, conv_b, bias, out, p, g,
                                                                   (int)pool, (hipStream_t)stream),
-                         "conv3d_div_maxpool_gap_bias_sum launch");
+                         what);
+}
+
+int conv3d_div_maxpool_gap_bias_sum(const float *x, const float *w, const float *conv_b,
+                                    float divisor, int64_t pool, const float *bias, float *out,
+                                    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                    int64_t Cout, int64_t k, void *stream)
+{
+    return pool_sum_entry("conv3d_div_maxpool_gap_bias_sum", false, x, w, conv_b, divisor, pool,
+                          bias, out, N, Cin, D, H, W, Cout, k, stream);
+}
+
+int conv3d_div_maxpool_gap_bias_sum_split_bf16(const float *x, const float *w,
+                                               const float *conv_b, float divisor, int64_t pool,
+                                               const float *bias, float *out, int64_t N,
+                                               int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                               int64_t Cout, int64_t k, void *stream)
+{
+    return pool_sum_entry("conv3d_div_maxpool_gap_bias_sum_split_bf16", true, x, w, conv_b,
+                          divisor, pool, bias, out, N, Cin, D, H, W, Cout, k, stream);
 }
 
 int conv3d_div_maxpool(const float *x, const float *w, const float *conv_b, float divisor,

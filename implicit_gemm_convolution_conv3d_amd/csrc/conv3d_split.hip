@@ -1,5 +1,6 @@
-// conv3d_split.hip -- Conv3d + Mish + tanh (k = 3, stride 1, pad <= 2) with the implicit GEMM
-// on bf16 matrix cores as a three-term split of fp32: the opt-in reduced-precision mode the
+// conv3d_split.hip -- Conv3d + Mish + tanh (k = 3, stride 1, pad <= 2) and the Conv3d +
+// divide + max-pool + channel-sum layer (k = 3, pool 2) with the implicit GEMM on bf16 matrix
+// cores as a three-term split of fp32: the opt-in reduced-precision mode the
 // pages weigh against true fp32 (page "Kimi-K2.6 l2_p47", the roofline estimate and the
 // mma-precision paragraph; gfx950 has no TF32-like format, so fp32 is emulated).  Each fp32
 // operand v splits into hi = bf16(v) and lo = bf16(v - hi); v*w is taken as
@@ -24,12 +25,19 @@ namespace {
 constexpr int kSpCC = 8;     // input channels per chunk: the 8 elements of a fragment
 constexpr int kSpSteps = 7;  // k-steps per chunk: 28 taps (27 + one with zero weights)
 
-template <int WD_, int WH_>
-struct SpGeom {
-    static constexpr int WD = WD_, WH = WH_, NT = 64 * WD * WH, NBW = 4;
-    static constexpr int HD = WD + 2, HH = WH + 2, RSX = 72;  // halo column c: ow0 - 4 + c
+// Split halo of NT threads: HD x HH rows of RSX positions, each 8 channels of hi and of lo.
+template <int NT_, int HD_, int HH_, int RSX_>
+struct SpHalo {
+    static constexpr int NT = NT_, HD = HD_, HH = HH_, RSX = RSX_;
     static constexpr int POS = HD * HH * RSX;                // halo positions
     static constexpr int PPT = (POS + NT - 1) / NT;          // positions per thread
+};
+
+// Conv3d tile: WD x WH waves, each one output row of 64 voxels; halo column c holds input
+// column ow0 - 4 + c.
+template <int WD_, int WH_>
+struct SpGeom : SpHalo<64 * WD_ * WH_, WD_ + 2, WH_ + 2, 72> {
+    static constexpr int WD = WD_, WH = WH_, NBW = 4;
 };
 
 // One chunk in registers between the global loads and the split LDS stores.
@@ -185,6 +193,125 @@ __global__ __launch_bounds__(64 * WD * WH, 8 / (WD * WH)) void conv3d_split_kern
     if (active) store_conv_row<MB, NBW, ACT, SW>(y, b, d, n, od, oh, ow0, o0, acc);
 }
 
+// ------------------------------------------------------------------ pooling layer
+// Conv3d (k = 3, no padding), divide, 2x2x2 max-pool, then the pooled channel sum (or, STORE,
+// the pooled tensor), with the Conv3d on the split.  Workgroup = WH waves; wave w owns pooled
+// row (n, pd0, ph0 + w), the 8*NBW pooled columns from pw0 and output channels
+// [o0, o0 + 16).  Its conv voxels come in 4*NBW blocks (dd, dh, q): conv voxel
+// (2*pd0 + dd, 2*(ph0 + w) + dh, 2*pw0 + 16*q + j) for MFMA row j.  Halo: 4 depth planes x
+// (2*WH + 2) rows x (16*NBW + 2) columns (column c holds input column 2*pw0 + c).  The voxels
+// are the MFMA rows, so a lane holds 4 consecutive conv columns of one channel: two whole
+// windows, whose maximum needs no other lane.
+template <int WH, int NBW>
+using SpPoolGeom = SpHalo<64 * WH, 4, 2 * WH + 2, 16 * NBW + 2>;
+
+template <int WH, int NBW, bool STORE>
+__global__ __launch_bounds__(64 * WH, 8 / WH) void conv3d_pool_split_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
+    float *__restrict__ out, PoolDims p, int64_t tiles, int tiles_w, int tiles_h,
+    float inv_count)
+{
+    using G = SpPoolGeom<WH, NBW>;
+    constexpr int NB = 4 * NBW;
+    constexpr int WENT = kSpSteps * 64;  // weight fragments per chunk (16 outputs)
+    __shared__ bf16x8 xs_hi[G::POS], xs_lo[G::POS];
+    __shared__ bf16x8 ws_hi[WENT], ws_lo[WENT];
+    const Conv3dDims &d = p.conv;
+
+    int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int tw = (int)(t % tiles_w); t /= tiles_w;
+    const int th = (int)(t % tiles_h); t /= tiles_h;
+    const int pd0 = (int)(t % p.PD); t /= p.PD;
+    const int64_t n = t % d.N;
+    const int o0 = (int)(t / d.N) * 16;
+    const int ph0 = th * WH, pw0 = tw * 8 * NBW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+
+    if (threadIdx.x < 16) {  // the 28th tap's weights are zero and never restaged
+        const int e = 6 * 64 + 48 + threadIdx.x;
+        ws_hi[e] = bf16x8{};
+        ws_lo[e] = bf16x8{};
+    }
+    // lane (g, j) at k-step s: halo (kd + dd, 2*wave + dh + kh, 16*q + j + kw) for tap
+    // 4s + g = (kd, kh, kw) of block (dd, dh, q); toff holds the part without (dd, dh, q)
+    int toff[kSpSteps];
+#pragma unroll
+    for (int s = 0; s < kSpSteps; ++s) {
+        const int tp = 4 * s + g < 27 ? 4 * s + g : 26;
+        const int kd = tp / 9, kh = (tp / 3) % 3, kw = tp % 3;
+        toff[s] = (kd * G::HH + 2 * wave + kh) * G::RSX + (lane & 15) + kw;
+    }
+
+    const int id0 = 2 * pd0, ih0 = 2 * ph0, iw0 = 2 * pw0;
+    const int ph = ph0 + wave;
+    const bool active = ph < p.PH;
+    floatx4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Each chunk is loaded right before it is stored (no prefetch: its registers would stay
+    // live through the MFMAs); the other resident workgroups cover the latency.
+    for (int c0 = 0; c0 < d.C; c0 += kSpCC) {
+        __syncthreads();
+        {
+            SpStage<1, G> stage;
+            stage.load(x, w, d, n, c0, o0, id0, ih0, iw0);
+            stage.store(xs_hi, xs_lo, reinterpret_cast<__bf16 *>(ws_hi),
+                        reinterpret_cast<__bf16 *>(ws_lo));
+        }
+        __syncthreads();
+        if (!active) continue;  // (this wave only helps stage the shared tiles)
+#pragma unroll
+        for (int s = 0; s < kSpSteps; ++s) {
+            const bf16x8 wh_ = ws_hi[s * 64 + lane], wl_ = ws_lo[s * 64 + lane];
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+                    for (int q = 0; q < NBW; ++q) {
+                        const int b = (dd * 2 + dh) * NBW + q;
+                        const int pos = toff[s] + (dd * G::HH + dh) * G::RSX + 16 * q;
+                        const bf16x8 xh = xs_hi[pos], xl = xs_lo[pos];
+                        acc[b] = mfma_16x16x32_bf16(xl, wh_, acc[b]);
+                        acc[b] = mfma_16x16x32_bf16(xh, wl_, acc[b]);
+                        acc[b] = mfma_16x16x32_bf16(xh, wh_, acc[b]);
+                    }
+        }
+    }
+    if (!active) return;  // (no barrier follows)
+    // (conv + cb) / divisor is monotone in conv: the window's extreme of the divided values is
+    // (max conv + cb) / divisor for a positive divisor, (min conv + cb) / divisor otherwise.
+    const bool use_min = p.divisor < 0.0f;
+    const int o = o0 + (lane & 15);
+    const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
+    float part = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NBW; ++q)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float m = acc[q][2 * half];
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float v = acc[b2 * NBW + q][2 * half + e];
+                    m = use_min ? fminf(m, v) : fmaxf(m, v);
+                }
+            const int pw = pw0 + 8 * q + 2 * g + half;
+            if (o < d.O && pw < p.PW) {
+                const float v = (m + cbv) / p.divisor;
+                if constexpr (STORE)
+                    out[(((n * d.O + o) * p.PD + pd0) * p.PH + ph) * p.PW + pw] = v;
+                else
+                    part += v;
+            }
+        }
+    if constexpr (!STORE) {
+        part = wave_sum(part);
+        if (lane == 0) atomicAdd(out + n, part * inv_count);
+    }
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <int MB, int WD, int WH, bool ACT>
@@ -207,6 +334,35 @@ hipError_t launch_split(const float *x, const float *w, const float *b, float *y
 }
 
 }  // namespace
+
+namespace {
+
+template <bool STORE>
+hipError_t launch_pool_split(const float *x, const float *w, const float *conv_b, float *out,
+                             const PoolDims &p, hipStream_t s)
+{
+    constexpr int WH = 4, NBW = 1;
+    const Conv3dDims &d = p.conv;
+    const int64_t tw = cdiv(p.PW, 8 * NBW), th = cdiv(p.PH, WH);
+    const int64_t tiles = tw * th * p.PD * d.N * cdiv(d.O, 16);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    hipLaunchKernelGGL((conv3d_pool_split_kernel<WH, NBW, STORE>), dim3((unsigned)tiles),
+                       dim3(64 * WH), 0, s, x, w, conv_b, out, p, tiles, (int)tw, (int)th,
+                       inv_count);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv3d_pool_sum_split_bf16(const float *x, const float *w,
+                                             const float *conv_b, const float *bias, float *out,
+                                             const PoolDims &p, hipStream_t s)
+{
+    const hipError_t e = launch_pool_sum_init(bias, out, p.conv.N, p.conv.O, s);
+    if (e != hipSuccess) return e;
+    return launch_pool_split<false>(x, w, conv_b, out, p, s);
+}
 
 hipError_t launch_conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b,
                                               float *y, const Conv3dDims &d, hipStream_t s)

@@ -89,7 +89,8 @@ class Workload:
         if self.op in ("conv3d_mish_tanh", "conv3d_mish_tanh_split_bf16"):
             return conv3d_act_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                      self.params["k"], bias=True)
-        if self.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool"):
+        if self.op in ("conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool",
+                       "conv3d_div_maxpool_gap_bias_sum_split_bf16"):
             return conv3d_pool_inputs(s, d["N"], d["C"], d["D"], d["H"], d["W"], d["O"],
                                       self.params["k"], conv_bias=True)
         if self.op in ("dwsep_conv2d", "dwsep_conv2d_split_bf16"):
@@ -133,4 +134,7 @@ WORKLOADS = {
                  dict(K=3, stride=1, pad=1, dilation=1, bias=True)),
     12: Workload(12, "conv3d_mish_tanh_split_bf16", "conv3d_mish_tanh_split_bf16",
                  dict(N=16, C=32, D=32, H=64, W=64, O=64), dict(k=3, stride=1, pad=0)),
+    13: Workload(13, "conv3d_div_maxpool_gap_bias_sum_split_bf16",
+                 "conv3d_div_maxpool_gap_bias_sum_split_bf16",
+                 dict(N=128, C=8, D=16, H=64, W=64, O=16), dict(k=3, divisor=2.0, pool=2)),
 }

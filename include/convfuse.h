@@ -142,6 +142,23 @@ int conv3d_mish_tanh_split_bf16(const float *x, const float *w, const float *b, 
                                 void *stream);
 
 /*
+ * conv3d_div_maxpool_gap_bias_sum with the Conv3d on bf16 matrix cores (opt-in precision
+ * mode, the same three-term split of fp32; divide, max-pool, mean, bias and sum in fp32).
+ * Error contract: each conv output v is off by at most 2^-14 * S(v), S(v) = the sum over taps
+ * and input channels of |x * w| (3 * 2^-16 per product).  A window maximum moves by at most
+ * the largest change in its window, a mean by at most the largest of its terms, so with
+ * M_o[n] = the largest S(v) over the pooled voxels of image n and output channel o,
+ *     |out[n] - out_exact[n]| <= 1e-4 |out_exact[n]| + 2^-14 * sum_o M_o[n] / |divisor|.
+ * Same arguments, layouts and errors as conv3d_div_maxpool_gap_bias_sum.  Applies to k = 3
+ * and pool 2; every other case runs the fp32 kernels.
+ */
+int conv3d_div_maxpool_gap_bias_sum_split_bf16(const float *x, const float *w,
+                                               const float *conv_b, float divisor, int64_t pool,
+                                               const float *bias, float *out, int64_t N,
+                                               int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                               int64_t Cout, int64_t k, void *stream);
+
+/*
  * dwsep_conv2d with the pointwise GEMM on bf16 matrix cores (opt-in precision mode).  The
  * pages weigh reduced-precision tensor-core formats (TF32) against true fp32 for these layers
  * (page "Kimi-K2.6 l2_p47", the roofline estimate and the mma-precision paragraph); gfx950 has

@@ -141,6 +141,23 @@ def test_conv3d_split_validation(kw, code):
     assert cf.lib().convfuse_last_error().decode().startswith("conv3d_mish_tanh_split_bf16")
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), cf.ERR_NULL), (dict(bias=None), cf.ERR_NULL), (dict(out=None), cf.ERR_NULL),
+    (dict(div=0.0), cf.ERR_SHAPE), (dict(div=float("nan")), cf.ERR_SHAPE), (dict(D=3), cf.ERR_SHAPE),
+    (dict(pool=0), cf.ERR_SHAPE), (dict(C=0), cf.ERR_SHAPE),
+    (dict(pool=33, D=66, H=66, W=66), cf.ERR_UNSUPPORTED),
+])
+def test_pool_split_validation(kw, code):
+    a = dict(x=FAKE, w=FAKE, cb=None, div=2.0, pool=2, bias=FAKE, out=FAKE, N=1, C=4, D=8, H=8,
+             W=8, O=8, k=3)
+    a.update(kw)
+    assert cf.lib().conv3d_div_maxpool_gap_bias_sum_split_bf16(
+        a["x"], a["w"], a["cb"], a["div"], a["pool"], a["bias"], a["out"], a["N"], a["C"],
+        a["D"], a["H"], a["W"], a["O"], a["k"], None) == code
+    assert cf.lib().convfuse_last_error().decode().startswith(
+        "conv3d_div_maxpool_gap_bias_sum_split_bf16")
+
+
 def call_dw_split(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W=8, O=8,
                   K=3, s=1, p=1, d=1):
     return cf.lib().dwsep_conv2d_split_bf16(x, dw, db, pw, pb, y, N, C, H, W, O, K, s, p, d, None)

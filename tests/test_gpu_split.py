@@ -210,3 +210,54 @@ def test_conv3d_split_full_workload_sampled():
     y2 = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
                                           p["stride"], p["pad"])
     assert bool(torch.equal(y, y2))
+
+
+POOL_SPLIT_CASES = [
+    # (N, C, D, H, W, O, divisor, conv_bias)
+    (2, 8, 8, 12, 20, 16, 2.0, True),     # one chunk, one channel group
+    (1, 13, 9, 21, 40, 20, -1.5, True),   # two chunks (ragged), two groups, negative divisor
+    (3, 4, 6, 6, 37, 5, 0.75, False),     # ragged pooled rows and columns, few channels
+]
+
+
+def pool_split_bound(inp, ref, divisor):
+    """1e-4 |ref| + 2^-14 * sum_o (largest sum |x*w| over the pooled voxels) / |divisor|."""
+    s = oracle.conv3d(np.abs(inp["x"]), np.abs(inp["w"]), None, 1, 0)
+    PD, PH, PW = (n // 2 for n in s.shape[2:])
+    m = s[:, :, :2 * PD, :2 * PH, :2 * PW].reshape(s.shape[0], s.shape[1], -1).max(axis=2)
+    return 1e-4 * np.abs(ref) + 2.0 ** -14 * m.sum(axis=1) / abs(divisor)
+
+
+@pytest.mark.parametrize("case", POOL_SPLIT_CASES)
+def test_pool_split_small(case):
+    N, C, D, H, W, O, div, cbias = case
+    inp = wl.conv3d_pool_inputs(740 + int(sum(case)), N, C, D, H, W, O, conv_bias=cbias)
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"], inp["w"], inp["conv_b"], div, 2,
+                                                 inp["bias"])
+    out = cf().conv3d_div_maxpool_gap_bias_sum_split_bf16(dev(inp["x"]), dev(inp["w"]),
+                                                          dev(inp["conv_b"]), div, 2,
+                                                          dev(inp["bias"]))
+    got = out.cpu().numpy().astype(np.float64)
+    bound = pool_split_bound(inp, ref, div)
+    assert np.all(np.abs(got - ref) <= bound), (case, got, ref, bound)
+
+
+def test_pool_split_full_workload_picks():
+    w = wl.WORKLOADS[13]
+    inp = w.inputs()
+    p = w.params
+    out = cf().conv3d_div_maxpool_gap_bias_sum_split_bf16(dev(inp["x"]), dev(inp["w"]),
+                                                          dev(inp["conv_b"]), p["divisor"],
+                                                          p["pool"], dev(inp["bias"]))
+    got = out.cpu().numpy().astype(np.float64)
+    picks = [0, 77, 127]
+    sub = dict(inp, x=inp["x"][picks])
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(sub["x"], inp["w"], inp["conv_b"],
+                                                 p["divisor"], p["pool"], inp["bias"])
+    bound = pool_split_bound(sub, ref, p["divisor"])
+    assert np.all(np.abs(got[picks] - ref) <= bound), (got[picks], ref, bound)
+    torch = _torch()
+    assert bool(torch.isfinite(out).all())
+    out32 = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
+                                                 p["divisor"], p["pool"], dev(inp["bias"]))
+    assert not bool(torch.equal(out, out32))
