@@ -73,7 +73,7 @@ int device_status(hipError_t e, const char *what)
 
 extern "C" {
 
-int convfuse_abi_version(void) { return 100; }
+int convfuse_abi_version(void) { return CONVFUSE_ABI_VERSION; }
 
 const char *convfuse_last_error(void) { return g_err; }
 

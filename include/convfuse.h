@@ -225,7 +225,10 @@ int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, in
  * pointer stays valid until the thread's next failing call. */
 const char *convfuse_last_error(void);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version (major * 100 + minor).  A caller built against this header can compare
+ * CONVFUSE_ABI_VERSION with what the loaded library returns; minor versions only add entry
+ * points (1.01 added the unfused steps' and the split-bf16 entry points). */
+#define CONVFUSE_ABI_VERSION 101
 int convfuse_abi_version(void);
 
 #ifdef __cplusplus

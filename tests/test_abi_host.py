@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = cf.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.convfuse_abi_version() == 100
+    assert L.convfuse_abi_version() == 101
 
 
 @pytest.mark.parametrize("args,expected", [
