@@ -2,8 +2,9 @@
 CPU oracle through the C ABI: the Conv3d kernels' plain-load staging (a chunk of input
 channels above 2^31 bytes), the chunked depthwise-separable kernel (pointwise weights too
 large for LDS, or an image above 2^31 bytes), the general kernels' direct fallbacks (kernel
-size above 7, a chunk beyond 32-bit offsets), and the split-bf16 mode's fp32 fallback.  Same
-tolerances as the other parity tests."""
+size above 7, a chunk beyond 32-bit offsets), the split-bf16 mode's fp32 fallback, and guard
+bands after outputs written by the float2 / float4 row epilogues.  Same tolerances as the
+other parity tests."""
 import numpy as np
 import pytest
 
@@ -91,3 +92,43 @@ def test_dwsep_general_direct_fallbacks():
     idx = edge_indices(y.shape, np.random.default_rng(7), 3000)
     ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], None, inp["pw_w"], None, idx, 2, 2, 1)
     assert_close(gather(y, idx), ref, "dwsep K5 s2 beyond 32-bit chunk offsets")
+
+
+@pytest.mark.parametrize("entry,shape,k,stride,pad", [
+    ("conv3d_mish_tanh", (1, 3, 5, 6, 16), 3, 1, 0),             # tuned, float2 rows, partial quad
+    ("conv3d_mish_tanh", (1, 3, 5, 6, 22), 3, 1, 2),             # tuned, float4 rows (OW = 24)
+    ("conv3d_mish_tanh", (1, 3, 9, 10, 26), 5, 2, 2),            # staged, OW = 13: single floats
+    ("conv3d_mish_tanh", (1, 3, 9, 10, 32), 5, 1, 2),            # staged, float4 rows
+    ("conv3d_mish_tanh_split_bf16", (1, 9, 5, 6, 16), 3, 1, 0),  # split, float2 rows
+])
+def test_conv3d_row_stores_stay_inside(entry, shape, k, stride, pad):
+    """A guard band after y stays untouched by the vector-store row epilogues."""
+    import torch
+    N, C, D, H, W = shape
+    O = 19
+    inp = wl.conv3d_act_inputs(930 + W, N, C, D, H, W, O, k=k)
+    od, oh, ow = ((s + 2 * pad - k) // stride + 1 for s in (D, H, W))
+    n_out = N * O * od * oh * ow
+    buf = torch.full((n_out + 4096,), 12345.0, device="cuda")
+    y = buf[:n_out].view(N, O, od, oh, ow)
+    getattr(cf(), entry)(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), stride, pad, out=y)
+    assert bool((buf[n_out:] == 12345.0).all())
+    ref = oracle.conv3d_mish_tanh(inp["x"], inp["w"], inp["b"], stride, pad)
+    if entry == "conv3d_mish_tanh":
+        assert_close(y.cpu().numpy(), ref, "guarded %s %s" % (entry, shape))
+    else:
+        assert np.all(np.abs(y.cpu().numpy() - ref) <= 1e-3)
+
+
+def test_dwsep_staged_stores_stay_inside():
+    import torch
+    inp = wl.dwsep_inputs(940, 1, 6, 9, 35, 21, K=5, bias=True)
+    ho, wo = 5, 18  # stride 2, pad 2
+    n_out = 21 * ho * wo
+    buf = torch.full((n_out + 4096,), 12345.0, device="cuda")
+    y = buf[:n_out].view(1, 21, ho, wo)
+    cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
+                      dev(inp["pw_b"]), 2, 2, 1, out=y)
+    assert bool((buf[n_out:] == 12345.0).all())
+    ref = oracle.dwsep_conv2d(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"], 2, 2, 1)
+    assert_close(y.cpu().numpy(), ref, "guarded staged dwsep")
