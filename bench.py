@@ -227,6 +227,16 @@ def cpu_baseline(workloads, frac_batch):
     return 2 * total_macs / secs / 1e12, oracle.threads(), desc
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def ablation(cf, wls, steps, warmup):
     """Fused entry point against the unfused path built from the same kernels (conv writing
     its output, then the epilogue or reduction as separate kernels; depthwise writing its
@@ -294,7 +304,7 @@ def ablation(cf, wls, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
@@ -386,10 +396,14 @@ def main():
         avg = float(times.mean())
         tfl = 2 * macs / (avg * 1e-3) / 1e12
         gbs = nbytes / (avg * 1e-3) / 1e9
+        fm, fh = tfl / PEAK_FP32_TFLOPS, gbs / PEAK_HBM_GBS
         per[w.name] = {
-            "op": w.op, "ms_avg": round(avg, 4), "ms_min": round(float(times.min()), 4),
-            "tflops": round(tfl, 2), "frac_fp32_mfma": round(tfl / PEAK_FP32_TFLOPS, 4),
-            "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "op": w.op, "kernel": kernel_name(w), "ms_avg": round(avg, 4),
+            "ms_median": round(float(np.median(times)), 4), "ms_min": round(float(times.min()), 4),
+            "tflops": round(tfl, 2), "frac_fp32_mfma": round(fm, 4),
+            "gbs": round(gbs, 1), "frac_hbm": round(fh, 4),
+            # the binding roof's fraction: max(flop / peak, bytes / bandwidth) / time
+            "frac_roofline": round(max(fm, fh), 4),
             "gflop": round(2 * macs / 1e9, 3), "mbytes": round(nbytes / 1e6, 2),
         }
         if avg > dom_ms:
@@ -410,7 +424,7 @@ def main():
         torch.cuda.empty_cache()
         v, cores, desc = cpu_baseline(wls, args.cpu_sample_frac)
         cpu = {"value": round(v, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-               "sample": desc}
+               "sample": desc, "cpu_model": cpu_model()}
 
     line = {
         "metric": "conv TFLOP/s (2xMACs) and % fp32 MFMA/HBM roofline per config, 1xMI355X",
