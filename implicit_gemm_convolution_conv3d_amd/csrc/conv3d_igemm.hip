@@ -5,11 +5,14 @@
 //     atomic per workgroup                  (page "Kimi-K2.6 l2_p8", the rewrite of the
 //                                            output as a sum of channel means plus sum(bias))
 //
-// GEMM view (page l2_p47, implicit-GEMM paragraph): rows = output channels, columns =
-// output voxels, reduction K = Cin * 27 ordered tap-major, channel-minor.  One k-step of
-// the 16x16x4 MFMA consumes four consecutive input channels at one tap, so the B operand
-// of lane l is the LDS halo value of channel (l/16) at voxel column (l%16) shifted by the
-// tap: its LDS address is a per-lane base plus a compile-time offset.
+// GEMM view (page l2_p47, implicit-GEMM paragraph): output channels x output voxels,
+// reduction K = Cin * 27 ordered tap-major, channel-minor.  One k-step of the 16x16x4 MFMA
+// consumes four consecutive input channels at one tap, so the voxel-side operand of lane l
+// is the LDS halo value of channel (l/16) at voxel column (l%16) shifted by the tap: its LDS
+// address is a per-lane base plus a compile-time offset.  The Mish/tanh kernel makes the
+// voxels the MFMA rows (each lane ends with 4 consecutive voxels of one channel, stored
+// together); the pool kernel makes the channels the rows (each lane ends with one voxel of 4
+// channels, and window columns pair up between neighbouring lanes).
 //
 // Workgroup = WD x WH waves.  Each wave owns a box of output voxels and all 16*MB output
 // channels of its channel group.  The input halo of the workgroup's box and the matching

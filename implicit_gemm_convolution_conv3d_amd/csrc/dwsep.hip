@@ -11,10 +11,10 @@
 //
 // Each wave owns R output rows x 16 pixel columns and every output channel of its channel
 // group, so the input is read once per channel group.  Workgroups are 4 waves wide (tile 64
-// columns) and WH waves tall.  Input channels stream through LDS in chunks of 16: thread t
-// stages channel (t/16)%16, column quad t%16 of its share of the halo rows (one float4 per
-// row when rows are 16-byte aligned, else four dwords); the next chunk is loaded into
-// registers while the current one computes.
+// columns) and WH waves tall.  Input channels stream through LDS in chunks of CC (32 when the
+// weights leave room, else 16): thread t stages channel (t/16)%CC, column quad t%16 of its
+// share of the halo rows (one float4 per row when rows are 16-byte aligned, else four
+// dwords); the next chunk is loaded into registers while the current one computes.
 //
 // Two kernels:
 //  * persistent (all pointwise weights and depthwise taps fit in LDS next to one chunk):
@@ -36,7 +36,7 @@ namespace convfuse {
 
 namespace {
 
-constexpr int kDwCC = 16;  // input channels per chunk
+constexpr int kDwCC = 16;  // input channels per chunk of the chunked kernel
 constexpr int kDwTW = 64;  // output tile width (4 waves x 16 columns)
 
 // Tile geometry: 4*WH waves, R output rows per wave, tile 64 columns x R*WH rows; CC input

@@ -7,9 +7,12 @@
 // padding of the Conv3d; page "Kimi-K2.6 l1_p86", stride/padding/dilation and kernel sizes
 // 1/3/5/7 of the depthwise-separable Conv2d; page "Kimi-K2.6 l2_p8", the pooled channel sum).
 //
-// Conv3d with kernel size 3, 5 or 7 and stride 1 or 2 (any padding) runs an LDS-staged
-// implicit GEMM with the tuned kernel's organisation (conv3d_staged_kernel).  Everything else
-// is a direct implicit GEMM over global memory: one wave owns 16*MB output channels x 16*NB
+// LDS-staged kernels cover the common cases: Conv3d with kernel size 3, 5 or 7 and stride 1
+// or 2, any padding (conv3d_staged_kernel, the tuned kernel's organisation); the pooled layer
+// with kernel size 1, 3 or 5 and pool 2, 3 or 4 (conv3d_pool_staged_kernel); the
+// depthwise-separable conv with any kernel size up to 7, stride and dilation
+// (dwsep_staged_kernel, input rows streamed straight into LDS).  Everything else is a
+// direct implicit GEMM over global memory: one wave owns 16*MB output channels x 16*NB
 // output positions along W, and each 16x16x4 MFMA k-step gathers its operands straight from
 // global memory (L1/L2 serve the reuse) with zero padding by bounds checks; there is no LDS
 // staging and no inter-wave synchronisation except the pooled sum's window reduction.
