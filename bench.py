@@ -227,6 +227,50 @@ def cpu_baseline(workloads, frac_batch):
     return 2 * total_macs / secs / 1e12, oracle.threads(), desc
 
 
+def ceilings(cf, reps):
+    """Practical ceilings on this GPU: the fp32 MFMA issue rate (convfuse_measure_mfma: 8
+    workgroups of 4 waves per CU, 16 independent accumulators per wave, no memory traffic)
+    and the HBM rate of torch's copy and fill over 1 GiB.  Median of `reps` launches each,
+    HIP events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    out = torch.zeros(1, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 8 * cus, 2048
+    t_mfma = timed(lambda: cf.measure_mfma(iters, wgs, out))
+    assert out.item() == iters * 2.0 ** -14  # the loop ran every MFMA
+    mfma_tf = wgs * 4 * iters * 16 * 2048 / (t_mfma * 1e-3) / 1e12
+    n = 1 << 28
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    t_fill = timed(lambda: dst.fill_(2.0))
+    res = {
+        "fp32_mfma_tflops": round(mfma_tf, 1),
+        "fp32_mfma_frac_of_spec": round(mfma_tf / PEAK_FP32_TFLOPS, 4),
+        "copy_gbs": round(8 * n / (t_copy * 1e-3) / 1e9, 1),
+        "fill_gbs": round(4 * n / (t_fill * 1e-3) / 1e9, 1),
+        "cus": cus,
+    }
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -319,6 +363,10 @@ def main():
                          "WRITE_SIZE) of runs that included --copy-calibration-mib into "
                          "profiles/traffic.json")
     ap.add_argument("--calibration-mib", type=int, default=1024)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the benchmark, measure the practical ceilings: an fp32 "
+                         "MFMA issue loop with no memory traffic, and torch copy / fill over "
+                         "1 GiB")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the benchmark, time each workload fused and unfused "
                          "(separate conv/epilogue/reduce or depthwise/pointwise kernels)")
@@ -353,6 +401,9 @@ def main():
     dev = torch.device("cuda:0")
     ids = [int(s) for s in args.workloads.split(",") if s]
     wls = [wl.WORKLOADS[i] for i in ids]
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(cf, args.steps)}), flush=True)
+        return
     if args.ablation:
         print(json.dumps({"ablation": ablation(cf, wls, args.steps, args.warmup),
                           "kernel_source_sha": kernel_source_sha()}), flush=True)

@@ -18,7 +18,7 @@ __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
-    "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len",
+    "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len", "measure_mfma",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
     "conv3d_div_maxpool_gap_bias_sum_split_bf16",
     "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
+    "convfuse_measure_mfma",
 )
 
 _lib = None
@@ -75,6 +76,7 @@ def lib():
             L.depthwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 8 + [_vp]
             L.pointwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 5 + [_vp]
             L.convfuse_conv_out_len.argtypes = [_i64] * 5 + [ctypes.POINTER(_i64)]
+            L.convfuse_measure_mfma.argtypes = [_vp, _i64, _i64, _vp]
             L.convfuse_last_error.restype = ctypes.c_char_p
             L.convfuse_abi_version.restype = ctypes.c_int
             for name in ("conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d",
@@ -87,6 +89,16 @@ def lib():
 def _check(rc):
     if rc != OK:
         raise ConvFuseError(rc, lib().convfuse_last_error().decode(errors="replace"))
+
+
+def measure_mfma(iters, workgroups, out):
+    """Diagnostic fp32 matrix-core issue loop (see convfuse_measure_mfma); out: 1-element
+    float32 CUDA tensor."""
+    import torch
+    with torch.cuda.device(out.device):
+        _check(lib().convfuse_measure_mfma(_ptr(out, "out", (1,)), iters, workgroups,
+                                           _stream(out)))
+    return out
 
 
 def conv_out_len(n, k, stride=1, pad=0, dilation=1):

@@ -75,6 +75,18 @@ extern "C" {
 
 int convfuse_abi_version(void) { return CONVFUSE_ABI_VERSION; }
 
+int convfuse_measure_mfma(float *out, int64_t iters, int64_t workgroups, void *stream)
+{
+    const char *fn = "convfuse_measure_mfma";
+    if (iters < 1 || iters >= ((int64_t)1 << 22) || workgroups < 1 || workgroups > (1 << 20))
+        return fail(CONVFUSE_ERR_SHAPE, "%s: iters must be in [1, 2^22), workgroups in [1, 2^20]",
+                    fn);
+    if (!out) return fail(CONVFUSE_ERR_NULL, "%s: out is required", fn);
+    return device_status(
+        convfuse::launch_mfma_loop(out, (int)iters, (int)workgroups, (hipStream_t)stream),
+        "convfuse_measure_mfma launch");
+}
+
 const char *convfuse_last_error(void) { return g_err; }
 
 int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dilation,

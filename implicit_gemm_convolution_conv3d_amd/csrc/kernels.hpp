@@ -63,6 +63,9 @@ hipError_t launch_pointwise_conv2d(const float *x, const float *pw_w, const floa
 
 // dwsep with the pointwise GEMM on bf16 matrix cores as a three-term split of each fp32
 // operand (opt-in precision mode; k = 3, stride 1, dilation 1, pad <= 2).
+// Diagnostic: workgroups x 4 waves, each running iters x 16 independent fp32 MFMAs.
+hipError_t launch_mfma_loop(float *out, int iters, int workgroups, hipStream_t stream);
+
 // Split-bf16 mode of conv3d_div_maxpool_gap_bias_sum (k = 3, pool 2).
 hipError_t launch_conv3d_pool_sum_split_bf16(const float *x, const float *w,
                                              const float *conv_b, const float *bias, float *out,

@@ -225,9 +225,19 @@ int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, in
  * pointer stays valid until the thread's next failing call. */
 const char *convfuse_last_error(void);
 
+/*
+ * Diagnostic, outside the convolution path: launches `workgroups` workgroups of 4 waves,
+ * each wave running iters x 16 independent fp32 16x16x4 MFMAs with no memory traffic, so
+ * the launch's rate (workgroups * 4 * iters * 16 * 2048 FLOP over its duration) is the
+ * practical fp32 matrix-core ceiling that the kernels' roofline fractions are compared
+ * with.  Writes iters * 2^-14 to out[0] (a device pointer), exactly.  Errors: SHAPE for
+ * iters outside [1, 2^22) or workgroups outside [1, 2^20], NULL for a null out.
+ */
+int convfuse_measure_mfma(float *out, int64_t iters, int64_t workgroups, void *stream);
+
 /* ABI version (major * 100 + minor).  A caller built against this header can compare
  * CONVFUSE_ABI_VERSION with what the loaded library returns; minor versions only add entry
- * points (1.01 added the unfused steps' and the split-bf16 entry points). */
+ * points (1.01 added the unfused steps', the split-bf16 and the diagnostic entry points). */
 #define CONVFUSE_ABI_VERSION 101
 int convfuse_abi_version(void);
 

@@ -158,6 +158,15 @@ def test_pool_split_validation(kw, code):
         "conv3d_div_maxpool_gap_bias_sum_split_bf16")
 
 
+@pytest.mark.parametrize("iters,wgs,out,code", [
+    (0, 1, FAKE, cf.ERR_SHAPE), (1 << 22, 1, FAKE, cf.ERR_SHAPE), (1, 0, FAKE, cf.ERR_SHAPE),
+    (1, (1 << 20) + 1, FAKE, cf.ERR_SHAPE), (1, 1, None, cf.ERR_NULL),
+])
+def test_measure_mfma_validation(iters, wgs, out, code):
+    assert cf.lib().convfuse_measure_mfma(out, iters, wgs, None) == code
+    assert cf.lib().convfuse_last_error().decode().startswith("convfuse_measure_mfma")
+
+
 def call_dw_split(x=FAKE, dw=FAKE, db=None, pw=FAKE, pb=None, y=FAKE, N=1, C=4, H=8, W=8, O=8,
                   K=3, s=1, p=1, d=1):
     return cf.lib().dwsep_conv2d_split_bf16(x, dw, db, pw, pb, y, N, C, H, W, O, K, s, p, d, None)
