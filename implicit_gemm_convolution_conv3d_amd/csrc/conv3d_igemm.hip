@@ -383,10 +383,17 @@ template <bool ACT>
 hipError_t launch_conv3d(const float *x, const float *w, const float *b, float *y,
                          const Conv3dDims &d, hipStream_t s)
 {
+    // 64 output channels per workgroup from 65 up; 32 from 17 to 64 (measured 1.7 % faster on
+    // the 64-channel layer: 4 workgroups fit per CU instead of 3, at the cost of staging the
+    // input twice from L2)
     const bool wide = d.OW > 16;
-    if (d.O > 16) {
+    if (d.O > 64) {
         if (wide) return launch_act<4, 4, 2, 2, 4, ACT>(x, w, b, y, d, s);
         return launch_act<4, 1, 2, 2, 4, ACT>(x, w, b, y, d, s);
+    }
+    if (d.O > 16) {
+        if (wide) return launch_act<2, 4, 2, 2, 4, ACT>(x, w, b, y, d, s);
+        return launch_act<2, 1, 2, 2, 4, ACT>(x, w, b, y, d, s);
     }
     if (wide) return launch_act<1, 4, 2, 2, 4, ACT>(x, w, b, y, d, s);
     return launch_act<1, 1, 2, 2, 4, ACT>(x, w, b, y, d, s);
