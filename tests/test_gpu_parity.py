@@ -214,6 +214,15 @@ DW_CASES = [
     (2, 4, 6, 20, 200, 2, True),           # padding 2, two channel groups
     (1, 4, 5, 19, 8, 0, False),            # no padding
     (1, 3, 1, 1, 5, 1, True),              # 1x1 image
+    # wider layers: weights near the LDS limit of the 32-channel-chunk persistent kernel
+    # (Cin 97-128) and the 16-channel-chunk persistent kernel (Cin 129-192)
+    (1, 100, 7, 37, 100, 1, True),         # 128-channel group, unaligned rows
+    (1, 110, 6, 40, 128, 1, False),        # the same, aligned rows
+    (1, 150, 6, 36, 128, 1, True),         # 16-channel chunks, aligned rows
+    (1, 120, 5, 21, 150, 1, True),         # 192-channel group, unaligned rows
+    (1, 140, 5, 24, 192, 1, False),        # 192-channel group, 16-channel chunks
+    (1, 200, 9, 44, 40, 1, True),          # 64-channel group, near the LDS limit
+    (1, 300, 5, 27, 64, 1, False),         # 64-channel group, 16-channel chunks
 ]
 
 

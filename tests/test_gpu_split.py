@@ -54,6 +54,10 @@ SPLIT_CASES = [
     (1, 4, 5, 19, 8, 0, False),            # no padding
     (1, 3, 1, 1, 5, 1, True),              # 1x1 image
     (3, 33, 10, 24, 70, 1, True),          # one channel past a k-step, 3 images
+    # split weights near the LDS limit
+    (1, 170, 6, 24, 100, 1, True),         # 128-channel group, aligned rows
+    (1, 110, 5, 21, 150, 1, True),         # 192-channel group, unaligned rows
+    (1, 330, 4, 20, 48, 1, False),         # 64-channel group
 ]
 
 
