@@ -266,35 +266,38 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
         }
         // (conv + cb) / divisor is monotone in conv: increasing for a positive divisor, so
         // the window maximum of the divided values is (max conv + cb) / divisor; for a
-        // negative divisor it is (min conv + cb) / divisor.
-        const bool use_min = pd_.divisor < 0.0f;
+        // negative divisor it is (min conv + cb) / divisor.  The direction is uniform, so
+        // each gets its own code.  The sum path adds the undivided (extreme + cb) and divides
+        // the workgroup's total once.
         const int j = lane & 15;
+        auto windows = [&](auto use_min) {
+            constexpr bool MIN = decltype(use_min)::value;
+            auto ext = [](float a, float b) { return MIN ? fminf(a, b) : fmaxf(a, b); };
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
-                const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    const int o = o0 + 16 * mb + 4 * (lane >> 4) + r;
+                    const float cbv = (cb && o < d.O) ? cb[o] : 0.0f;
 #pragma unroll
-                for (int q = 0; q < NBW; ++q) {
-                    float m = acc[mb][q][r];
+                    for (int q = 0; q < NBW; ++q) {
+                        float m = acc[mb][q][r];
 #pragma unroll
-                    for (int p = 1; p < 4; ++p) {
-                        const float v = acc[mb][p * NBW + q][r];
-                        m = use_min ? fminf(m, v) : fmaxf(m, v);
-                    }
-                    const float m2 = __shfl_xor(m, 1, 64);
-                    m = use_min ? fminf(m, m2) : fmaxf(m, m2);
-                    const int pw = pw0 + 8 * q + (j >> 1);
-                    if (o < d.O && (j & 1) == 0 && pw < pd_.PW) {
-                        const float v = (m + cbv) / pd_.divisor;
-                        if constexpr (STORE)
-                            out[(((n * d.O + o) * pd_.PD + pdi) * pd_.PH + phi) * pd_.PW + pw] = v;
-                        else
-                            part += v;
+                        for (int p = 1; p < 4; ++p) m = ext(m, acc[mb][p * NBW + q][r]);
+                        m = ext(m, __shfl_xor(m, 1, 64));
+                        const int pw = pw0 + 8 * q + (j >> 1);
+                        if (o < d.O && (j & 1) == 0 && pw < pd_.PW) {
+                            if constexpr (STORE)
+                                out[(((n * d.O + o) * pd_.PD + pdi) * pd_.PH + phi) * pd_.PW + pw] =
+                                    (m + cbv) / pd_.divisor;
+                            else
+                                part += m + cbv;
+                        }
                     }
                 }
-            }
+        };
+        if (pd_.divisor < 0.0f) windows(std::true_type{});
+        else windows(std::false_type{});
     } else {
         for (int c0 = 0; c0 < d.C; c0 += CC) {
             __syncthreads();
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_pool_sum_kernel(
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < NT / 64; ++i) s += red[i];
-        atomicAdd(out + n, s * inv_count);
+        atomicAdd(out + n, s * inv_count / pd_.divisor);
     }
 }
 
