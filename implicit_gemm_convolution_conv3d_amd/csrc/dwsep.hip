@@ -174,37 +174,46 @@ struct DwHaloStager {
     }
 };
 
-// One chunk of the K loop.  xs: halo of the chunk, lane base applied; pw: fragment-order
-// pointwise weights of the chunk's first k-step, lane base applied (pw[cg*64*MB + mb] is the
-// operand of k-step cg, output block mb); dk: depthwise taps [c][12] (9 taps, bias at 9) of
-// the chunk's channel 4*cg + lane/16 at dk[cg*48].
+// One chunk of the K loop, reading LDS array `lds` at per-lane float offsets: xoff, the
+// chunk's halo (channel lane/16 of k-step 0 at the lane's pixel column, tap (0, 0)); poff,
+// the chunk's fragment-order pointwise weights (lds[poff + cg*64*MB + mb] is the operand of
+// k-step cg, output block mb); doff, the depthwise taps [c][12] (9 taps, bias at 9) of the
+// chunk's channel lane/16 (channel 4*cg + lane/16 at doff + 48*cg).  The offsets are opaque
+// to the optimiser, so each read is one base register plus an immediate offset: the weights
+// lie beyond the 16-bit immediate range from the start of LDS, and folding the region start
+// into every read costs a vector add per read.
 // DW = false: pointwise only (the unfused path's second pass); the operand is the staged
 // input itself, x at the centre tap of the K = 3, pad 1 halo.
 template <int MB, int R, int RS, int CS, int CC, bool PIXROWS, bool DW = true>
-__device__ __forceinline__ void dw_chunk(const float *xs, const float *pw, const float *dk,
+__device__ __forceinline__ void dw_chunk(const float *lds, int xoff, int poff, int doff,
                                          floatx4 (&acc)[MB][R])
 {
+    asm volatile("" : "+v"(poff), "+v"(doff));
 #pragma unroll
     for (int cg = 0; cg < CC / 4; ++cg) {
-        const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg);
-        const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 4);
-        const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dk + 48 * cg + 8);
+        const floatx4 k0 = *reinterpret_cast<const floatx4 *>(lds + doff + 48 * cg);
+        const floatx4 k1 = *reinterpret_cast<const floatx4 *>(lds + doff + 48 * cg + 4);
+        const floatx4 k2 = *reinterpret_cast<const floatx4 *>(lds + doff + 48 * cg + 8);
         const float kw9[9] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3], k2[0]};
         const float dbias = k2[1];
         float pwf[MB];
 #pragma unroll
         for (int i = 0; i < MB / 4; ++i) {
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(pw + cg * 64 * MB + 4 * i);
+            const floatx4 v =
+                *reinterpret_cast<const floatx4 *>(lds + poff + cg * 64 * MB + 4 * i);
             pwf[4 * i + 0] = v[0];
             pwf[4 * i + 1] = v[1];
             pwf[4 * i + 2] = v[2];
             pwf[4 * i + 3] = v[3];
         }
         float xv[R + 2][3];
+        // one base per k-step; the R + 2 rows x 3 taps are immediate offsets from it
+        int xo = xoff + 4 * cg * CS;
+        asm volatile("" : "+v"(xo));
 #pragma unroll
         for (int hr = 0; hr < R + 2; ++hr)
 #pragma unroll
-            for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = xs[4 * cg * CS + hr * RS + kw];
+            for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = lds[xo + hr * RS + kw];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float v = xv[r + 1][1];
@@ -474,8 +483,9 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
                 lc = 0;
             }
             if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc);
-            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS, DW>(xl, pl + (c0 / 4) * 64 * MB,
-                                                           dl + c0 * 12, acc);
+            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS, DW>(
+                dyn, (int)(xl - dyn), (int)(pl - dyn) + (c0 / 4) * 64 * MB,
+                (int)(dl - dyn) + c0 * 12, acc);
             if (last) break;
             lds_barrier();
             hs.store(xs, k);
@@ -775,7 +785,8 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
                 hs.load(k, x, d, n, h0, w0, c0 + kDwCC);
                 wload(wc, c0 + kDwCC);
             }
-            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS, DW>(xl, pl, dl, acc);
+            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS, DW>(lds, (int)(xl - lds), (int)(pl - lds),
+                                                              (int)(dl - lds), acc);
         }
         dw_epilogue<MB, R, PIXROWS>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
     } else {
