@@ -25,10 +25,12 @@
 //    next tile computes.
 //  * chunked (any size): one tile per workgroup, weights staged with every chunk.
 //
-// PIXROWS selects which MFMA operand carries the pixels.  With pixels as the A operand each
-// lane ends with 4 consecutive pixels of one output channel and stores them as one float4
-// (rows 16-byte aligned); otherwise each lane holds 4 output channels of one pixel and the
-// 16 lanes of a row group store 64 contiguous bytes.
+// Operand roles: the pointwise weights are the MFMA's A operand and the depthwise outputs
+// (pixels) its B operand, so each lane ends with 4 output channels of one pixel and a store
+// instruction writes 4 channels x 64 contiguous bytes.  With the roles swapped each lane
+// would hold 4 consecutive pixels of one channel and could store float4s, 16 channels x 64
+// bytes per instruction; on the 512 x 512 layer that order measured 6-9 % slower (the output
+// stream reaches HBM more slowly when each store touches 16 channel planes).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -184,7 +186,7 @@ struct DwHaloStager {
 // into every read costs a vector add per read.
 // DW = false: pointwise only (the unfused path's second pass); the operand is the staged
 // input itself, x at the centre tap of the K = 3, pad 1 halo.
-template <int MB, int R, int RS, int CS, int CC, bool PIXROWS, bool DW = true>
+template <int MB, int R, int RS, int CS, int CC, bool DW = true>
 __device__ __forceinline__ void dw_chunk(const float *lds, int xoff, int poff, int doff,
                                          floatx4 (&acc)[MB][R])
 {
@@ -225,82 +227,49 @@ __device__ __forceinline__ void dw_chunk(const float *lds, int xoff, int poff, i
                     for (int kw = 0; kw < 3; ++kw) v = fmaf(kw9[kh * 3 + kw], xv[r + kh][kw], v);
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                if constexpr (PIXROWS)
-                    acc[mb][r] = mfma_16x16x4(v, pwf[mb], acc[mb][r]);
-                else
-                    acc[mb][r] = mfma_16x16x4(pwf[mb], v, acc[mb][r]);
-            }
+            for (int mb = 0; mb < MB; ++mb) acc[mb][r] = mfma_16x16x4(pwf[mb], v, acc[mb][r]);
         }
     }
 }
 
-// Store one wave's R x 16 outputs of output channels [obase, obase + ocnt).
-template <int MB, int R, bool PIXROWS>
+// Store one wave's R x 16 outputs of output channels [obase, obase + ocnt): lane holds
+// channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16.
+template <int MB, int R>
 __device__ __forceinline__ void dw_epilogue(float *__restrict__ y, const DwsepDims &d, int64_t n,
                                             int hbase, int wcol0, int obase, int ocnt,
                                             const floatx4 (&acc)[MB][R])
 {
     const int lane = threadIdx.x & 63;
-    if constexpr (PIXROWS) {
-        // lane holds pixels wcol0 + 4*(lane/16) + 0..3 of channel 16*mb + lane%16
-        const int wcol = wcol0 + 4 * (lane >> 4);
+    const int wcol = wcol0 + (lane & 15);
+    if (wcol >= d.Wo) return;
+    int64_t cstride = (int64_t)d.Ho * d.Wo;
+    // Opaque to the optimiser: keeps the per-channel offsets from being hoisted out of the
+    // caller's tile loop, where they would pin dozens of scalar registers.
+    asm volatile("" : "+s"(cstride));
+    float *yp = y + ((n * d.O + obase + 4 * (lane >> 4)) * d.Ho + hbase) * d.Wo + wcol;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int ol = 16 * mb + (lane & 15);
-            if (ol >= ocnt) continue;
-            float *yp = y + ((n * d.O + obase + ol) * d.Ho + hbase) * d.Wo + wcol;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (hbase + r >= d.Ho) continue;
-                if (wcol + 3 < d.Wo) {
-                    *reinterpret_cast<floatx4 *>(yp + (int64_t)r * d.Wo) = acc[mb][r];
-                } else {
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int ol = 16 * mb + 4 * (lane >> 4) + r4;
+            if (ol < ocnt) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (wcol + i < d.Wo) yp[(int64_t)r * d.Wo + i] = acc[mb][r][i];
-                }
+                for (int r = 0; r < R; ++r)
+                    if (hbase + r < d.Ho) yp[(int64_t)r * d.Wo] = acc[mb][r][r4];
             }
+            yp += r4 == 3 ? 13 * cstride : cstride;
         }
-    } else {
-        // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16
-        const int wcol = wcol0 + (lane & 15);
-        if (wcol >= d.Wo) return;
-        int64_t cstride = (int64_t)d.Ho * d.Wo;
-        // Opaque to the optimiser: keeps the per-channel offsets from being hoisted out of
-        // the caller's tile loop, where they would pin dozens of scalar registers.
-        asm volatile("" : "+s"(cstride));
-        float *yp = y + ((n * d.O + obase + 4 * (lane >> 4)) * d.Ho + hbase) * d.Wo + wcol;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int ol = 16 * mb + 4 * (lane >> 4) + r4;
-                if (ol < ocnt) {
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        if (hbase + r < d.Ho) yp[(int64_t)r * d.Wo] = acc[mb][r][r4];
-                }
-                yp += r4 == 3 ? 13 * cstride : cstride;
-            }
-    }
 }
 
 // Accumulators start at the pointwise bias.  bs[16*mb + j] is the bias of output channel
 // obase + 16*mb + j (0 past the slice or without bias).
-template <int MB, int R, bool PIXROWS>
+template <int MB, int R>
 __device__ __forceinline__ void acc_init(floatx4 (&acc)[MB][R], const float *bs)
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        floatx4 b;
-        if constexpr (PIXROWS) {
-            const float v = bs[16 * mb + (lane & 15)];
-            b = floatx4{v, v, v, v};
-        } else {
-            b = *reinterpret_cast<const floatx4 *>(bs + 16 * mb + 4 * (lane >> 4));
-        }
+        const floatx4 b = *reinterpret_cast<const floatx4 *>(bs + 16 * mb + 4 * (lane >> 4));
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[mb][r] = b;
     }
@@ -310,7 +279,7 @@ __device__ __forceinline__ void acc_init(floatx4 (&acc)[MB][R], const float *bs)
 // Store one wave's R x 16 outputs of output channels [obase, obase + ocnt): tb points at
 // (n, obase, row h0, column 0); the wave's rows start at h0 + hrow0, its columns at wcol0.
 // Byte offsets from tb stay below 2^31 (checked by the host).
-template <int MB, int R, bool PIXROWS>
+template <int MB, int R>
 __device__ __forceinline__ void dw_epilogue_buf(float *tb, const DwsepDims &d, int hrow0,
                                                 int hleft, int wcol0, int ocnt,
                                                 const floatx4 (&acc)[MB][R])
@@ -322,40 +291,24 @@ __device__ __forceinline__ void dw_epilogue_buf(float *tb, const DwsepDims &d, i
     // Opaque to the optimiser: keeps the per-store offsets and lane masks from being hoisted
     // out of the caller's tile loop, where they would pin dozens of scalar registers.
     asm volatile("" : "+s"(plane), "+s"(wo), "+s"(ocnt));
-    if constexpr (PIXROWS) {
-        // lane holds pixels wcol0 + 4*(lane/16) + 0..3 of channel 16*mb + lane%16
-        // (output rows are 16-byte aligned and Wo % 4 == 0: a quad is wholly in or out)
-        const int wcol = wcol0 + 4 * (lane >> 4);
-        const int vbase = 4 * ((lane & 15) * plane + hrow0 * wo + wcol);
+    // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16
+    const int wcol = wcol0 + (lane & 15);
+    int vmb = 4 * (4 * (lane >> 4) * plane + hrow0 * wo + wcol);  // channel block mb
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const bool ok = 16 * mb + (lane & 15) < ocnt && r < hleft && wcol < wo;
-                const int off = ok ? vbase + 4 * (16 * mb * plane + r * wo) : kDropOffset;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mb][r]), rs,
-                                                       off, 0, 0);
+                const bool ok = 16 * mb + 4 * (lane >> 4) + r4 < ocnt && r < hleft && wcol < wo;
+                const int off = ok ? vmb + 4 * (r4 * plane + r * wo) : kDropOffset;
+                // (a vector element is copied out first: bit-casting the element expression
+                // itself would reinterpret the vector's first element)
+                const float v = acc[mb][r][r4];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
             }
-    } else {
-        // lane holds channels 16*mb + 4*(lane/16) + 0..3 of pixel wcol0 + lane%16
-        const int wcol = wcol0 + (lane & 15);
-        int vmb = 4 * (4 * (lane >> 4) * plane + hrow0 * wo + wcol);  // channel block mb
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const bool ok = 16 * mb + 4 * (lane >> 4) + r4 < ocnt && r < hleft && wcol < wo;
-                    const int off = ok ? vmb + 4 * (r4 * plane + r * wo) : kDropOffset;
-                    // (a vector element is copied out first: bit-casting the element
-                    // expression itself would reinterpret the vector's first element)
-                    const float v = acc[mb][r][r4];
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
-                }
-            vmb += 64 * plane;
-            asm volatile("" : "+v"(vmb));  // one running offset, not MB*4*R folded constants
-        }
+        vmb += 64 * plane;
+        asm volatile("" : "+v"(vmb));  // one running offset, not MB*4*R folded constants
     }
 }
 
@@ -389,7 +342,7 @@ constexpr size_t dw_weight_floats(int64_t C)
     return (size_t)(KS * 64 * MB + 4 * KS * 12 + 16 * MB);
 }
 
-template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS, bool DW>
+template <int MB, int R, int WH, int CC, bool VEC, bool DW>
 __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
@@ -467,7 +420,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
     lds_barrier();
     floatx4 acc[MB][R];
     for (;;) {
-        acc_init<MB, R, PIXROWS>(acc, bs);
+        acc_init<MB, R>(acc, bs);
         const int64_t ntile = tile + gridDim.x;
         int64_t nn = 0;
         int nh0 = 0, nw0 = 0;
@@ -483,7 +436,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
                 lc = 0;
             }
             if (!last || ntile < tiles) hs.load(k, x, d, ln, lh, lw, lc);
-            dw_chunk<MB, R, G::RS, G::CS, CC, PIXROWS, DW>(
+            dw_chunk<MB, R, G::RS, G::CS, CC, DW>(
                 dyn, (int)(xl - dyn), (int)(pl - dyn) + (c0 / 4) * 64 * MB,
                 (int)(dl - dyn) + c0 * 12, acc);
             if (last) break;
@@ -492,7 +445,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
             lds_barrier();
         }
         float *tb = y + ((n * d.O + obase) * d.Ho + h0) * d.Wo;
-        dw_epilogue_buf<MB, R, PIXROWS>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
+        dw_epilogue_buf<MB, R>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
                                         ocnt, acc);
         if (ntile >= tiles) break;
         tile = ntile;
@@ -511,7 +464,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
 // hi_v*hi_w + hi_v*lo_w + lo_v*hi_w with fp32 accumulation (the dropped lo*lo term and the
 // split residuals are below 2^-15 of |v*w|).  The depthwise step stays fp32 on the vector
 // ALUs.  One 16x16x32 bf16 k-step covers a 32-channel chunk: lane group g = lane/16 holds
-// the channels g + 4i (i = 0..7) of its pixel (A) or output channel (B), so the four groups
+// the channels g + 4i (i = 0..7) of its output channel (A) or pixel (B), so the four groups
 // read four different LDS bank groups of the halo.  Same tiles, staging, prefetch and
 // epilogue as the persistent fp32 kernel.
 // LDS bytes of the split kernel's weights: pointwise hi and lo fragments (KS k-steps of 32
@@ -523,7 +476,7 @@ constexpr size_t split_weight_bytes(int64_t C)
     return (size_t)(2 * KS * 64 * MB * 16 + KS * 32 * 12 * 4 + 16 * MB * 4);
 }
 
-template <int MB, int R, int WH, bool VEC, bool PIXROWS>
+template <int MB, int R, int WH, bool VEC>
 __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
@@ -592,12 +545,20 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
 
     // One chunk = one k-step: depthwise of the lane's 8 channels for each of its R rows,
     // split, then three bf16 MFMAs per (output block, row).
+    // LDS reads as one base register plus immediate offsets (the offsets are opaque to the
+    // optimiser; the weights lie beyond the 16-bit immediate range from the start of LDS)
+    const int xoff = (int)(xl - dyn);
     auto chunk = [&](int st, floatx4 (&acc)[MB][R]) {
+        int doff = (int)(dl - dyn) + 32 * st * 12;
+        int pho = (int)(reinterpret_cast<const float *>(pwh + (st * 64 + lane) * MB) - dyn);
+        int plo = (int)(reinterpret_cast<const float *>(pwl + (st * 64 + lane) * MB) - dyn);
+        asm volatile("" : "+v"(doff), "+v"(pho), "+v"(plo));
         float dw[R][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float *xc = xl + 4 * i * G::CS;
-            const float *dk = dl + (32 * st + 4 * i) * 12;
+            int xo = xoff + 4 * i * G::CS;
+            asm volatile("" : "+v"(xo));
+            const float *dk = dyn + doff + 48 * i;
             const floatx4 k0 = *reinterpret_cast<const floatx4 *>(dk);
             const floatx4 k1 = *reinterpret_cast<const floatx4 *>(dk + 4);
             const floatx4 k2 = *reinterpret_cast<const floatx4 *>(dk + 8);
@@ -606,7 +567,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
 #pragma unroll
             for (int hr = 0; hr < R + 2; ++hr)
 #pragma unroll
-                for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = xc[hr * G::RS + kw];
+                for (int kw = 0; kw < 3; ++kw) xv[hr][kw] = dyn[xo + hr * G::RS + kw];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float v = k2[1];
@@ -617,8 +578,8 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
                 dw[r][i] = v;
             }
         }
-        const bf16x8 *ph = pwh + (st * 64 + lane) * MB;
-        const bf16x8 *pl = pwl + (st * 64 + lane) * MB;
+        const bf16x8 *ph = reinterpret_cast<const bf16x8 *>(dyn + pho);
+        const bf16x8 *pl = reinterpret_cast<const bf16x8 *>(dyn + plo);
         bf16x8 dhs[R], dls[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) split_bf16(dw[r], dhs[r], dls[r]);
@@ -628,15 +589,9 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const bf16x8 dh = dhs[r], dlo = dls[r];
-                if constexpr (PIXROWS) {
-                    acc[mb][r] = mfma_16x16x32_bf16(dlo, wh_, acc[mb][r]);
-                    acc[mb][r] = mfma_16x16x32_bf16(dh, wl_, acc[mb][r]);
-                    acc[mb][r] = mfma_16x16x32_bf16(dh, wh_, acc[mb][r]);
-                } else {
-                    acc[mb][r] = mfma_16x16x32_bf16(wh_, dlo, acc[mb][r]);
-                    acc[mb][r] = mfma_16x16x32_bf16(wl_, dh, acc[mb][r]);
-                    acc[mb][r] = mfma_16x16x32_bf16(wh_, dh, acc[mb][r]);
-                }
+                acc[mb][r] = mfma_16x16x32_bf16(wh_, dlo, acc[mb][r]);
+                acc[mb][r] = mfma_16x16x32_bf16(wl_, dh, acc[mb][r]);
+                acc[mb][r] = mfma_16x16x32_bf16(wh_, dh, acc[mb][r]);
             }
         }
     };
@@ -651,7 +606,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
     lds_barrier();
     floatx4 acc[MB][R];
     for (;;) {
-        acc_init<MB, R, PIXROWS>(acc, bs);
+        acc_init<MB, R>(acc, bs);
         const int64_t ntile = tile + gridDim.x;
         int64_t nn = 0;
         int nh0 = 0, nw0 = 0;
@@ -674,7 +629,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_split_kernel(
             lds_barrier();
         }
         float *tb = y + ((n * d.O + obase) * d.Ho + h0) * d.Wo;
-        dw_epilogue_buf<MB, R, PIXROWS>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
+        dw_epilogue_buf<MB, R>(tb, d, R * wh, (int)(d.Ho - h0) - R * wh, w0 + 16 * ww,
                                         ocnt, acc);
         if (ntile >= tiles) break;
         tile = ntile;
@@ -698,7 +653,7 @@ struct DwWeightChunk {
     float dw;
 };
 
-template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
+template <int MB, int R, bool VEC, bool DW>
 __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
     const float *__restrict__ x, const float *__restrict__ dw_w, const float *__restrict__ dw_b,
     const float *__restrict__ pw_w, const float *__restrict__ pw_b, float *__restrict__ y,
@@ -780,15 +735,15 @@ __global__ __launch_bounds__(256, 2) void dwsep_chunked_kernel(
             hs.store(xs, k);
             wstore(wc);
             lds_barrier();
-            if (c0 == 0) acc_init<MB, R, PIXROWS>(acc, bs);
+            if (c0 == 0) acc_init<MB, R>(acc, bs);
             if (c0 + kDwCC < C) {
                 hs.load(k, x, d, n, h0, w0, c0 + kDwCC);
                 wload(wc, c0 + kDwCC);
             }
-            dw_chunk<MB, R, G::RS, G::CS, kDwCC, PIXROWS, DW>(lds, (int)(xl - lds), (int)(pl - lds),
+            dw_chunk<MB, R, G::RS, G::CS, kDwCC, DW>(lds, (int)(xl - lds), (int)(pl - lds),
                                                               (int)(dl - lds), acc);
         }
-        dw_epilogue<MB, R, PIXROWS>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
+        dw_epilogue<MB, R>(y, d, n, h0, w0 + 16 * wave, obase, ocnt, acc);
     } else {
         // This wave's columns lie past the output: it only helps stage the shared tiles.
         for (int c0 = 0; c0 < C; c0 += kDwCC) {
@@ -818,13 +773,13 @@ int cu_count()
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <int MB, int R, int WH, int CC, bool VEC, bool PIXROWS, bool DW>
+template <int MB, int R, int WH, int CC, bool VEC, bool DW>
 hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_b,
                              const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
                              int obase, size_t lds, int per_cu, hipStream_t s)
 {
     using G = DwGeom<R, WH, CC>;
-    auto kern = dwsep_persistent_kernel<MB, R, WH, CC, VEC, PIXROWS, DW>;
+    auto kern = dwsep_persistent_kernel<MB, R, WH, CC, VEC, DW>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -840,7 +795,7 @@ hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_
     return hipGetLastError();
 }
 
-template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
+template <int MB, int R, bool VEC, bool DW>
 hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                           const float *pw_b, float *y, const DwsepDims &d, int obase,
                           hipStream_t s)
@@ -848,7 +803,7 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
     const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, R);
     const int64_t tiles = tw * th * d.N;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, PIXROWS, DW>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, DW>), dim3((unsigned)tiles),
                        dim3(256), 0, s, x, dw_w, dw_b, pw_w, pw_b, y, d, obase, tiles, (int)tw,
                        (int)th);
     return hipGetLastError();
@@ -858,7 +813,7 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
 // kernel with one 8-wave workgroup per CU and 32-channel chunks when its weights and halo fit
 // in LDS, else with 16-channel chunks (two 4-wave workgroups per CU, or one 8-wave one), else
 // the chunked kernel.
-template <int MB, int R, bool VEC, bool PIXROWS, bool DW>
+template <int MB, int R, bool VEC, bool DW>
 hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                         const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
@@ -870,30 +825,26 @@ hipError_t launch_slice(const float *x, const float *dw_w, const float *dw_b, co
     const bool small_planes =
         64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
     if (small_planes && lds_a <= kLdsBytes)
-        return launch_persistent<MB, R, 2, 32, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 2, 32, VEC, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_a, 1, s);
     if (small_planes && 2 * lds_b <= kLdsBytes)
-        return launch_persistent<MB, R, 1, 16, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 1, 16, VEC, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_b, 2, s);
     if (small_planes && lds_c <= kLdsBytes)
-        return launch_persistent<MB, R, 2, 16, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
+        return launch_persistent<MB, R, 2, 16, VEC, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d,
                                                              obase, lds_c, 1, s);
-    return launch_chunked<MB, 2, VEC, PIXROWS, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    return launch_chunked<MB, 2, VEC, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
 }
 
 template <int MB, int R, bool DW>
 hipError_t launch(const float *x, const float *dw_w, const float *dw_b, const float *pw_w,
                   const float *pw_b, float *y, const DwsepDims &d, int obase, hipStream_t s)
 {
-    // float4 loads need 16-byte aligned input and pointwise rows; float4 stores need
-    // 16-byte aligned output rows.
+    // float4 loads need 16-byte aligned input and pointwise rows.
     const bool vin = d.W % 4 == 0 && d.C % 4 == 0 && ((uintptr_t)x & 15) == 0 &&
                      ((uintptr_t)pw_w & 15) == 0;
-    const bool vout = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
-    if (vin && vout) return launch_slice<MB, R, true, true, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    if (vin) return launch_slice<MB, R, true, false, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    if (vout) return launch_slice<MB, R, false, true, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
-    return launch_slice<MB, R, false, false, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    if (vin) return launch_slice<MB, R, true, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
+    return launch_slice<MB, R, false, DW>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, s);
 }
 
 }  // namespace
@@ -928,13 +879,13 @@ hipError_t launch_dwsep_conv2d(const float *x, const float *dw_w, const float *d
 
 namespace {
 
-template <int MB, int R, bool VEC, bool PIXROWS>
+template <int MB, int R, bool VEC>
 hipError_t launch_split_kernel(const float *x, const float *dw_w, const float *dw_b,
                                const float *pw_w, const float *pw_b, float *y, const DwsepDims &d,
                                int obase, size_t lds, hipStream_t s)
 {
     using G = DwGeom<R, 2, 32>;
-    auto kern = dwsep_split_kernel<MB, R, 2, VEC, PIXROWS>;
+    auto kern = dwsep_split_kernel<MB, R, 2, VEC>;
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -961,11 +912,8 @@ bool launch_split_slice(const float *x, const float *dw_w, const float *dw_b, co
         64 * MB * d.Ho * d.Wo <= kBufRange && 4 * d.C * d.H * d.W <= kBufRange;
     if (!small_planes || lds > kLdsBytes) return false;
     const bool vin = d.W % 4 == 0 && ((uintptr_t)x & 15) == 0;
-    const bool vout = d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0;
-    if (vin && vout) err = launch_split_kernel<MB, R, true, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
-    else if (vin) err = launch_split_kernel<MB, R, true, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
-    else if (vout) err = launch_split_kernel<MB, R, false, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
-    else err = launch_split_kernel<MB, R, false, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    if (vin) err = launch_split_kernel<MB, R, true>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
+    else err = launch_split_kernel<MB, R, false>(x, dw_w, dw_b, pw_w, pw_b, y, d, obase, lds, s);
     return true;
 }
 

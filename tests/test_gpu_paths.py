@@ -39,8 +39,8 @@ def test_pool_plain_load_staging():
 
 CHUNKED_CASES = [
     # (N, C, H, W, O, bias): 520 input channels, pointwise weights above the LDS size
-    (1, 520, 9, 70, 40, True),      # unaligned rows, channel-rows epilogue
-    (2, 520, 6, 72, 24, False),     # aligned rows, pixel-rows epilogue
+    (1, 520, 9, 70, 40, True),      # unaligned rows (scalar staging loads)
+    (2, 520, 6, 72, 24, False),     # aligned rows (float4 staging loads)
     (1, 516, 5, 33, 150, True),     # three output-channel groups
 ]
 
