@@ -29,8 +29,9 @@
 // (pixels) its B operand, so each lane ends with 4 output channels of one pixel and a store
 // instruction writes 4 channels x 64 contiguous bytes.  With the roles swapped each lane
 // would hold 4 consecutive pixels of one channel and could store float4s, 16 channels x 64
-// bytes per instruction; on the 512 x 512 layer that order measured 6-9 % slower (the output
-// stream reaches HBM more slowly when each store touches 16 channel planes).
+// bytes per instruction; on the 512 x 512 layer that order measured 6-9 % slower in this
+// kernel, although a store-only test writes it faster: the difference comes from how the
+// stores interleave with the halo loads and the matrix work, not from the raw write rate.
 #include "common.hpp"
 #include "kernels.hpp"
 
