@@ -677,33 +677,41 @@ __global__ __launch_bounds__(256, 2) void dwsep_staged_kernel(
     const int qcol = qa + 4 * lane;
     const bool qok = lane < nq && (unsigned)qcol < (unsigned)W;
 
-    // Issue the input rows of chunk c0 into buffer xsb (row r: channel r / HR, row r % HR).
+    // Issue the input rows of chunk c0 into buffer xsb: wave w copies every row of channels
+    // CPW*w .. CPW*w + CPW-1.  The wave index is made explicitly uniform, so each row's global
+    // offset and LDS address are scalar values and a row costs one vector select.
     // Byte offsets over the channels [c0, c0 + 8) of image n stay below 2^31 (host check).
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     auto rows_dma = [&](int c0, float *xsb) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(x + (n * C + c0) * (int64_t)H * W);
-        constexpr int CH = kDwsCC;
-        for (int r = wave; r < CH * g.HR; r += 4) {
-            const int cl = r / g.HR, hr = r - cl * g.HR;
-            const int ih = ih0 + hr;
-            const bool rowok = c0 + cl < C && (unsigned)ih < (unsigned)H;
-            const int rowoff = (cl * H + ih) * W;
-            float *dst = xsb + cl * g.CS + hr * g.RS;
-            if (g.vin) {
-                const int off = rowok && qok ? 4 * (rowoff + qcol) : kDropOffset;
-                if (lane < nq)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rs, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
-            } else {
+        constexpr int CPW = kDwsCC / 4;  // channels per wave (4 waves)
+        static_assert(kDwsCC % 4 == 0, "whole channels per wave");
 #pragma unroll
-                for (int jj = 0; jj < kDwsCPL; ++jj) {
-                    if (64 * jj >= span) break;
-                    const int col = 64 * jj + lane, iw = qa + col;
-                    const int off =
-                        rowok && (unsigned)iw < (unsigned)W ? 4 * (rowoff + iw) : kDropOffset;
-                    if (col < span)
+        for (int k = 0; k < CPW; ++k) {
+#pragma unroll
+            for (int hr = 0; hr < g.HR; ++hr) {
+                const int cl = CPW * wv + k;
+                const int ih = ih0 + hr;
+                const bool rowok = c0 + cl < C && (unsigned)ih < (unsigned)H;
+                const int rowoff = (cl * H + ih) * W;
+                float *dst = xsb + cl * g.CS + hr * g.RS;
+                if (g.vin) {
+                    const int off = rowok && qok ? 4 * (rowoff + qcol) : kDropOffset;
+                    if (lane < nq)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            rs, (__attribute__((address_space(3))) void *)(dst + 64 * jj), 4, off,
-                            0, 0, 0);
+                            rs, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < kDwsCPL; ++jj) {
+                        if (64 * jj >= span) break;
+                        const int col = 64 * jj + lane, iw = qa + col;
+                        const int off =
+                            rowok && (unsigned)iw < (unsigned)W ? 4 * (rowoff + iw) : kDropOffset;
+                        if (col < span)
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                rs, (__attribute__((address_space(3))) void *)(dst + 64 * jj), 4,
+                                off, 0, 0, 0);
+                    }
                 }
             }
         }
