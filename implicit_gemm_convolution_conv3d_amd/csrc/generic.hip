@@ -310,7 +310,9 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
 {
     using G = PoolGeom<K, P, NBW>;
     extern __shared__ __attribute__((aligned(16))) float dyn[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // (the wave index made explicitly uniform: the row copy's per-row decomposition and
+    // offsets are then scalar work)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     float *red = dyn + 2 * G::BUF + wave * G::RED;
     const Conv3dDims &d = p.conv;
     const int D = (int)d.D, H = (int)d.H, W = (int)d.W;
