@@ -376,7 +376,8 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(batch sharding needs no communication; see DESIGN.md). Run with --gpus 1.",
+              "(each batch item is independent, so batch sharding needs no communication). "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
