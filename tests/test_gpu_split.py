@@ -58,6 +58,9 @@ SPLIT_CASES = [
     (1, 170, 6, 24, 100, 1, True),         # 128-channel group, aligned rows
     (1, 110, 5, 21, 150, 1, True),         # 192-channel group, unaligned rows
     (1, 330, 4, 20, 48, 1, False),         # 64-channel group
+    # tall images: more tiles than workgroups, so workgroups take several tiles each
+    (2, 40, 600, 130, 100, 1, True),       # two chunks, ragged unaligned columns, 2 images
+    (1, 48, 1100, 64, 64, 2, True),        # padding 2
 ]
 
 
