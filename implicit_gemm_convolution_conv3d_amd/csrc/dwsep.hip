@@ -119,7 +119,14 @@ struct DwHaloStager {
                     const int off = rok && col < W ? base + 4 * hr * W : kDropOffset;
                     k.xr[i] = __builtin_bit_cast(
                         floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                } else if (col + 4 <= W) {
+                    // rows only 4-byte aligned: buffer loads need dword alignment only, so a
+                    // quad inside the row is still one 16-byte load
+                    const int off = rok ? base + 4 * hr * W : kDropOffset;
+                    k.xr[i] = __builtin_bit_cast(
+                        floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
                 } else {
+                    // the quad the row end cuts (or one past it): single loads, none beyond W
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int off = rok && col + e < W ? base + 4 * (hr * W + e) : kDropOffset;
