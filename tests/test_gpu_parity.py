@@ -70,6 +70,7 @@ ACT_CASES = [
     (1, 8, 5, 6, 20, 80, 1, False),        # two channel groups, padding 1, no bias
     (2, 3, 4, 4, 4, 16, 2, True),          # padding 2, output larger than input
     (1, 4, 3, 3, 3, 3, 0, True),           # single output voxel
+    (1, 8, 5, 6, 133, 32, 1, True),        # rows 4-byte aligned only, three W tiles
 ]
 
 
