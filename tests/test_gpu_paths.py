@@ -78,6 +78,24 @@ def test_dwsep_large_image():
     assert_close(gather(y, idx), ref, "dwsep large image")
 
 
+def test_dwsep_image_at_offset_limit():
+    """64 channels of 2048 x 4095 pixels: 2 146 959 360 bytes, just inside the 32-bit buffer
+    range, so the persistent kernel runs; its rows are only 4-byte aligned, so it stages with
+    16-byte loads inside each row and single loads where the row ends, up to the last row of
+    the range; sampled outputs and every corner."""
+    inp = wl.dwsep_inputs(922, 1, 64, 2048, 4095, 16, bias=True)
+    assert 4 * inp["x"].size < 2 ** 31 - 1
+    y = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
+                          dev(inp["pw_b"]))
+    idx = edge_indices(y.shape, np.random.default_rng(7), 4000)
+    # every output channel at the last 2 rows x 32 columns, which read the end of the range
+    o, h, w = np.meshgrid(np.arange(16), [2046, 2047], np.arange(4063, 4095), indexing="ij")
+    tail = np.ravel_multi_index((o.ravel(), h.ravel(), w.ravel()), (16, 2048, 4095))
+    idx = np.unique(np.concatenate([idx, tail]))
+    ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"], idx)
+    assert_close(gather(y, idx), ref, "dwsep image at the offset limit")
+
+
 def test_dwsep_general_direct_fallbacks():
     # kernel size 9: above the staged kernel's 7
     inp = wl.dwsep_inputs(922, 1, 6, 20, 30, 10, K=9, bias=True)
