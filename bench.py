@@ -7,10 +7,17 @@ One step = one call of each entry point on its full-size workload, in this order
   dwsep_conv2d                     x [16,64,512,512]       -> y [16,128,512,512]
   dwsep_conv2d (odd, biased)       x [8,96,333,517]        -> y [8,192,333,517]
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
-`value` is the step's convolution work (2 x multiply-adds) per second, in TFLOP/s.
-Each launch is also timed with HIP events on the stream it runs on; the per-workload
-numbers, the roofline fraction of the dominant kernel and a CPU-oracle baseline on a
-bounded sample are printed on the same JSON line.
+`value` is the step's convolution work (2 x multiply-adds) per second, in TFLOP/s, over
+`--steps` timed steps; each launch in them is also timed with HIP events on its stream (the
+`roofline` object uses those averages).  After the timed steps every workload is launched
+alone `--reps` times with the caches flushed before each launch (a 512 MiB write, then a
+512 MiB read of another buffer: the headline per-workload time is the median of these) and
+`--reps` times back to back (the warm median); the tiny configuration [1,4,8,16,16] is timed
+the same way over `--tiny-reps` launches (reported, not graded).  Each workload's record gives
+its rates against the fp32 matrix peak (matrix-core FLOP only: the depthwise step of the
+separable layers runs on the vector ALUs and is listed apart) and against HBM, and the roof
+it is graded on.  The CPU baseline runs the fp64 oracle over the same workloads, with the
+wall time of each.
 """
 from __future__ import annotations
 
@@ -76,6 +83,24 @@ def work(w):
     return macs, nbytes
 
 
+def gemm_macs(w):
+    """The multiply-adds that run as a matrix contraction on the fp32 matrix cores: the whole
+    Conv3d, but only the pointwise step of a depthwise-separable layer (its depthwise step
+    runs on the vector ALUs)."""
+    macs, _ = work(w)
+    if w.op.startswith("dwsep_conv2d"):
+        K = w.params["K"]
+        ho, wo = out_dims(w)
+        macs -= w.dims["N"] * ho * wo * w.dims["C"] * K * K
+    return macs
+
+
+def graded_bound(w):
+    """The roof a layer is judged against: HBM for the depthwise-separable layers, the fp32
+    matrix cores for the Conv3d layers."""
+    return "hbm" if w.op.startswith("dwsep_conv2d") else "mfma"
+
+
 def kernel_name(w):
     """The kernel a workload's entry point launches (the launchers' dispatch rules)."""
     p = w.params
@@ -99,12 +124,9 @@ def kernel_name(w):
 
 
 def kernel_source_sha():
-    h = hashlib.sha256()
-    csrc = ROOT / "implicit_gemm_convolution_conv3d_amd" / "csrc"
-    for f in sorted(csrc.glob("*")):
-        h.update(f.name.encode())
-        h.update(f.read_bytes())
-    return h.hexdigest()[:16]
+    """Source hash the loaded libconvfuse.so was compiled from (stamped in by the build)."""
+    import implicit_gemm_convolution_conv3d_amd as cf
+    return cf.build_id()
 
 
 def load_traffic(kernel_name):
@@ -199,9 +221,10 @@ def out_shape(w):
 
 def cpu_baseline(workloads, frac_batch):
     """The fp64 oracle, untouched, on the first batch items of each workload.  Input
-    generation is outside the timed region.  Returns (TFLOP/s, threads, description)."""
+    generation is outside the timed region.  Returns (TFLOP/s over all of them, threads,
+    description, per-workload {wall_s, gflop, gflops, batch_items})."""
     import oracle
-    total_macs, secs, parts = 0, 0.0, []
+    total_macs, secs, parts, per = 0, 0.0, [], {}
     for w in workloads:
         d, p = w.dims, w.params
         nb = max(1, int(round(d["N"] * frac_batch)))
@@ -219,12 +242,17 @@ def cpu_baseline(workloads, frac_batch):
         else:
             oracle.dwsep_conv2d(x, inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
                                 p["stride"], p["pad"], p["dilation"])
-        secs += time.perf_counter() - t0
-        total_macs += macs * nb // d["N"]
+        dt = time.perf_counter() - t0
+        secs += dt
+        m = macs * nb // d["N"]
+        total_macs += m
+        per[w.name] = {"wall_s": round(dt, 3), "gflop": round(2 * m / 1e9, 3),
+                       "gflops": round(2 * m / dt / 1e9, 2),
+                       "batch_items": "%d of %d" % (nb, d["N"])}
         parts.append("%s batch items 0..%d of %d" % (w.name, nb - 1, d["N"]))
         del inp, x
     desc = "; ".join(parts) + " (%.1f s of fp64 naive loops)" % secs
-    return 2 * total_macs / secs / 1e12, oracle.threads(), desc
+    return 2 * total_macs / secs / 1e12, oracle.threads(), desc, per
 
 
 def ceilings(cf, reps):
@@ -271,14 +299,24 @@ def ceilings(cf, reps):
     return res
 
 
-def cpu_model():
+def host_info():
+    """The host the CPU baseline ran on: the full model string and identifiers from
+    /proc/cpuinfo, the cores this process may use, and the OpenMP thread setting."""
+    info = {"cpu_model": "unknown"}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "model name" and info["cpu_model"] == "unknown":
+                info["cpu_model"] = val
+            elif key in ("vendor_id", "cpu family", "model", "stepping") and key not in info:
+                info[key.replace(" ", "_")] = val
     except OSError:
         pass
-    return "unknown"
+    info["nproc"] = len(os.sched_getaffinity(0))
+    info["os_cpu_count"] = os.cpu_count()
+    info["OMP_NUM_THREADS"] = os.environ.get("OMP_NUM_THREADS")
+    return info
 
 
 def ablation(cf, wls, steps, warmup):
@@ -350,6 +388,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20,
+                    help="launches per workload for the cold and the warm figures")
+    ap.add_argument("--tiny-reps", type=int, default=200,
+                    help="launches of the tiny configuration (0: skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of each workload's batch the oracle baseline runs on")
@@ -438,45 +480,54 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    per = {}
-    step_macs = 0
-    dominant, dom_ms = None, -1.0
-    for i, w in enumerate(wls):
-        times = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
-        macs, nbytes = work(w)
-        step_macs += macs
-        avg = float(times.mean())
-        tfl = 2 * macs / (avg * 1e-3) / 1e12
-        gbs = nbytes / (avg * 1e-3) / 1e9
-        fm, fh = tfl / PEAK_FP32_TFLOPS, gbs / PEAK_HBM_GBS
-        per[w.name] = {
-            "op": w.op, "kernel": kernel_name(w), "ms_avg": round(avg, 4),
-            "ms_median": round(float(np.median(times)), 4), "ms_min": round(float(times.min()), 4),
-            "tflops": round(tfl, 2), "frac_fp32_mfma": round(fm, 4),
-            "gbs": round(gbs, 1), "frac_hbm": round(fh, 4),
-            # the binding roof's fraction: max(flop / peak, bytes / bandwidth) / time
-            "frac_roofline": round(max(fm, fh), 4),
-            "gflop": round(2 * macs / 1e9, 3), "mbytes": round(nbytes / 1e6, 2),
-        }
-        if avg > dom_ms:
-            dominant, dom_ms = w, avg
+    step_ms = {w.name: np.array([ev[s][i][0].elapsed_time(ev[s][i][1])
+                                 for s in range(args.steps)]) for i, w in enumerate(wls)}
+    step_macs = sum(work(w)[0] for w in wls)
     value = 2 * step_macs / (ms_per_step * 1e-3) / 1e12
 
-    dmacs, dbytes = work(dominant)
-    kname = kernel_name(dominant)
+    # Per-workload figures, after the timed steps: each workload alone, `reps` launches with
+    # the cache flushed before each (cold, the headline) and `reps` back-to-back (warm).
+    flush = Flusher(torch, dev)
+    per = {}
+    for w, t, o in zip(wls, tensors, outs):
+        cold = launch_times(torch, stream, lambda: run_op(cf, w, t, o), args.reps, flush)
+        warm = launch_times(torch, stream, lambda: run_op(cf, w, t, o), args.reps, None)
+        per[w.name] = workload_figures(w, cold, warm, step_ms[w.name])
+    if args.tiny_reps and 1 not in ids:
+        # the tiny configuration: launch-bound, reported but not graded on throughput
+        w1 = wl.WORKLOADS[1]
+        t1 = {k: (None if v is None else torch.from_numpy(v).to(dev))
+              for k, v in w1.inputs().items()}
+        o1 = torch.empty(out_shape(w1), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            run_op(cf, w1, t1, o1)
+        cold = launch_times(torch, stream, lambda: run_op(cf, w1, t1, o1), args.tiny_reps, flush)
+        warm = launch_times(torch, stream, lambda: run_op(cf, w1, t1, o1), args.tiny_reps, None)
+        per[w1.name] = workload_figures(w1, cold, warm, None)
+        del t1, o1
+    del flush
+
+    # the roofline object: the kernel with the longest time in the timed steps, its
+    # algorithmic FLOP per launch over its average launch time there
+    dominant = max(wls, key=lambda w: float(step_ms[w.name].mean()))
+    dom_ms = float(step_ms[dominant.name].mean())
+    dmacs, _ = work(dominant)
     achieved = 2 * dmacs / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-                "traffic": load_traffic(dominant.name), "kernel": kname,
+                "traffic": load_traffic(dominant.name), "kernel": kernel_name(dominant),
                 "workload": dominant.name}
 
     cpu = None
     if not args.no_cpu_baseline:
         del tensors, outs
         torch.cuda.empty_cache()
-        v, cores, desc = cpu_baseline(wls, args.cpu_sample_frac)
+        base = list(wls)
+        if args.tiny_reps and 1 not in ids:
+            base = [wl.WORKLOADS[1]] + base
+        v, cores, desc, cpu_per = cpu_baseline(base, args.cpu_sample_frac)
         cpu = {"value": round(v, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-               "sample": desc, "cpu_model": cpu_model()}
+               "sample": desc, "per_workload": cpu_per, **host_info()}
 
     line = {
         "metric": "conv TFLOP/s (2xMACs) and % fp32 MFMA/HBM roofline per config, 1xMI355X",
@@ -489,6 +540,76 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+FLUSH_BYTES = 512 << 20   # twice the 256 MB last-level (MALL) cache
+
+
+class Flusher:
+    """Empties the caches between timed launches: writes one 512 MiB buffer, then reads
+    another 512 MiB, so the caches end up holding clean lines of an unrelated buffer (a write
+    alone would leave dirty lines that the timed kernel would have to write back)."""
+
+    def __init__(self, torch, dev):
+        self.w = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.r = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.s = torch.empty((), dtype=torch.float32, device=dev)
+        self.torch = torch
+
+    def __call__(self, rep):
+        self.w.fill_(float(rep))
+        self.torch.sum(self.r, out=self.s)
+
+
+def launch_times(torch, stream, fn, reps, flush):
+    """Milliseconds of `reps` launches of fn, each between two HIP events on the launch
+    stream; flush (if given) runs before each launch, outside its events."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    fn()
+    for r, (a, b) in enumerate(ev):
+        if flush is not None:
+            flush(r)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def workload_figures(w, cold, warm, step):
+    """Per-workload record: the cold median is the headline time; rates and roofline
+    fractions are computed from it."""
+    macs, nbytes = work(w)
+    gmacs = gemm_macs(w)
+    med = float(np.median(cold))
+    sec = med * 1e-3
+    fm = 2 * gmacs / sec / 1e12 / PEAK_FP32_TFLOPS
+    fh = nbytes / sec / 1e9 / PEAK_HBM_GBS
+    rec = {
+        "op": w.op, "kernel": kernel_name(w), "reps": int(cold.size),
+        "ms_median": round(med, 4), "ms_min": round(float(cold.min()), 4),
+        "ms_mean": round(float(cold.mean()), 4),
+        "ms_warm_median": round(float(np.median(warm)), 4),
+        "ms_in_step_mean": None if step is None else round(float(step.mean()), 4),
+        "tflops": round(2 * macs / sec / 1e12, 2),
+        "gflop": round(2 * macs / 1e9, 3),
+        "mfma_gflop": round(2 * gmacs / 1e9, 3),
+        "vector_gflop": round(2 * (macs - gmacs) / 1e9, 3),
+        "frac_fp32_mfma": round(fm, 4),
+        "gbs": round(nbytes / sec / 1e9, 1), "mbytes": round(nbytes / 1e6, 2),
+        "frac_hbm": round(fh, 4),
+        # max(matrix FLOP / matrix peak, bytes / HBM peak) / time
+        "frac_roofline": round(max(fm, fh), 4),
+    }
+    if w.index == 1:
+        rec["graded"] = None  # launch-bound: parity only
+    else:
+        bound = graded_bound(w)
+        frac, target = (fh, 0.60) if bound == "hbm" else (fm, 0.50)
+        rec["graded"] = {"bound": bound, "frac": round(frac, 4), "target": target,
+                         "met": bool(frac >= target)}
+    return rec
 
 
 if __name__ == "__main__":

@@ -18,7 +18,8 @@ __all__ = [
     "conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "conv3d_div_maxpool", "dwsep_conv2d",
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
-    "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len", "measure_mfma",
+    "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len", "out_dims_conv3d",
+    "out_dims_conv2d", "build_id", "measure_mfma",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -31,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
     "conv3d_div_maxpool_gap_bias_sum_split_bf16",
-    "convfuse_conv_out_len", "convfuse_last_error", "convfuse_abi_version",
+    "convfuse_conv_out_len", "convfuse_out_dims_conv3d", "convfuse_out_dims_conv2d",
+    "convfuse_build_id", "convfuse_last_error", "convfuse_abi_version",
     "convfuse_measure_mfma",
 )
 
@@ -52,13 +54,21 @@ def library_path():
 
 
 def lib():
-    """The loaded libconvfuse.so (built in-tree first if it does not exist yet)."""
+    """The loaded libconvfuse.so (built in-tree first if it does not exist yet).  Raises if
+    the binary was compiled from other sources than the ones in this tree."""
     global _lib
     with _lock:
         if _lib is None:
             if not _build.LIB.exists():
                 _build.build()
             L = ctypes.CDLL(str(_build.LIB))
+            L.convfuse_build_id.restype = ctypes.c_char_p
+            built, want = L.convfuse_build_id().decode(), _build.source_sha()
+            if built != want:
+                raise RuntimeError(
+                    "%s was built from sources %s, but the tree holds %s: rebuild it "
+                    "(python -m implicit_gemm_convolution_conv3d_amd._build)"
+                    % (_build.LIB, built, want))
             L.conv3d_mish_tanh.argtypes = [_vp] * 4 + [_i64] * 9 + [_vp]
             L.conv3d_div_maxpool_gap_bias_sum.argtypes = (
                 [_vp] * 3 + [ctypes.c_float, _i64, _vp, _vp] + [_i64] * 7 + [_vp])
@@ -76,6 +86,8 @@ def lib():
             L.depthwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 8 + [_vp]
             L.pointwise_conv2d.argtypes = [_vp] * 4 + [_i64] * 5 + [_vp]
             L.convfuse_conv_out_len.argtypes = [_i64] * 5 + [ctypes.POINTER(_i64)]
+            L.convfuse_out_dims_conv3d.argtypes = [_i64] * 6 + [ctypes.POINTER(_i64)] * 3
+            L.convfuse_out_dims_conv2d.argtypes = [_i64] * 6 + [ctypes.POINTER(_i64)] * 2
             L.convfuse_measure_mfma.argtypes = [_vp, _i64, _i64, _vp]
             L.convfuse_last_error.restype = ctypes.c_char_p
             L.convfuse_abi_version.restype = ctypes.c_int
@@ -105,6 +117,26 @@ def conv_out_len(n, k, stride=1, pad=0, dilation=1):
     out = _i64()
     _check(lib().convfuse_conv_out_len(n, k, stride, pad, dilation, ctypes.byref(out)))
     return out.value
+
+
+def out_dims_conv3d(D, H, W, k, stride=1, pad=0):
+    """(OD, OH, OW) of a Conv3d (convfuse_out_dims_conv3d)."""
+    o = [_i64() for _ in range(3)]
+    _check(lib().convfuse_out_dims_conv3d(D, H, W, k, stride, pad, *map(ctypes.byref, o)))
+    return tuple(v.value for v in o)
+
+
+def out_dims_conv2d(H, W, K, stride=1, pad=0, dilation=1):
+    """(Ho, Wo) of the depthwise step of a depthwise-separable Conv2d
+    (convfuse_out_dims_conv2d)."""
+    o = [_i64() for _ in range(2)]
+    _check(lib().convfuse_out_dims_conv2d(H, W, K, stride, pad, dilation, *map(ctypes.byref, o)))
+    return tuple(v.value for v in o)
+
+
+def build_id():
+    """Source hash the loaded library was compiled from (convfuse_build_id)."""
+    return lib().convfuse_build_id().decode()
 
 
 def _ptr(t, name, shape=None):
@@ -143,7 +175,7 @@ def conv3d_mish_tanh(x, w, b=None, stride=1, padding=0, out=None, _entry="conv3d
         raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
     if b is not None and tuple(b.shape) != (O,):
         raise ValueError("bias must have shape (%d,)" % O)
-    shp = (N, O) + tuple(conv_out_len(s, k, stride, padding) for s in (D, H, W))
+    shp = (N, O) + out_dims_conv3d(D, H, W, k, stride, padding)
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
@@ -220,8 +252,7 @@ def dwsep_conv2d(x, dw_w, dw_b, pw_w, pw_b, stride=1, padding=1, dilation=1, out
         raise ValueError("dw_b must have shape (%d,)" % C)
     if pw_b is not None and tuple(pw_b.shape) != (O,):
         raise ValueError("pw_b must have shape (%d,)" % O)
-    shp = (N, O, conv_out_len(H, K, stride, padding, dilation),
-           conv_out_len(W, K, stride, padding, dilation))
+    shp = (N, O) + out_dims_conv2d(H, W, K, stride, padding, dilation)
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
@@ -241,7 +272,7 @@ def conv3d_bias(x, w, b=None, stride=1, padding=0, out=None):
         raise ValueError("weight %s does not match input %s" % (tuple(w.shape), tuple(x.shape)))
     if b is not None and tuple(b.shape) != (O,):
         raise ValueError("bias must have shape (%d,)" % O)
-    shp = (N, O) + tuple(conv_out_len(s, k, stride, padding) for s in (D, H, W))
+    shp = (N, O) + out_dims_conv3d(D, H, W, k, stride, padding)
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
@@ -283,8 +314,7 @@ def depthwise_conv2d(x, dw_w, dw_b=None, stride=1, padding=1, dilation=1, out=No
     K = dw_w.shape[-1]
     if tuple(dw_w.shape) != (C, 1, K, K):
         raise ValueError("dw_w %s does not match input %s" % (tuple(dw_w.shape), tuple(x.shape)))
-    shp = (N, C, conv_out_len(H, K, stride, padding, dilation),
-           conv_out_len(W, K, stride, padding, dilation))
+    shp = (N, C) + out_dims_conv2d(H, W, K, stride, padding, dilation)
     if out is None:
         out = torch.empty(shp, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):

@@ -1,6 +1,7 @@
 """Build libconvfuse.so (the gfx950 kernels and the C ABI) in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -37,6 +38,16 @@ def _headers():
     return sorted(CSRC.glob("*.hpp")) + [ROOT / "include" / "convfuse.h"]
 
 
+def source_sha() -> str:
+    """Hash of every file the library is compiled from (csrc/ and the C header), 16 hex
+    digits.  The build stamps it into the binary (convfuse_build_id)."""
+    h = hashlib.sha256()
+    for f in sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.hpp")) + [ROOT / "include" / "convfuse.h"]:
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
 def stale() -> bool:
     if not LIB.exists():
         return True
@@ -50,10 +61,12 @@ def build(force: bool = False, verbose: bool = False) -> Path:
         return LIB
     BUILD_DIR.mkdir(exist_ok=True)
     cc = hipcc()
+    sha = source_sha()
 
     def compile_one(src: Path) -> Path:
         obj = BUILD_DIR / (src.stem + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-I", str(ROOT / "include"), "-c", str(src), "-o", str(obj)]
+        cmd = [cc, *HIPCC_FLAGS, '-DCONVFUSE_SOURCE_SHA="%s"' % sha, "-I", str(ROOT / "include"),
+               "-c", str(src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -104,6 +104,46 @@ int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, in
     return CONVFUSE_OK;
 }
 
+int convfuse_out_dims_conv3d(int64_t D, int64_t H, int64_t W, int64_t k, int64_t stride,
+                             int64_t pad, int64_t *OD, int64_t *OH, int64_t *OW)
+{
+    const char *fn = "convfuse_out_dims_conv3d";
+    if (!OD || !OH || !OW) return fail(CONVFUSE_ERR_NULL, "%s: OD, OH and OW are required", fn);
+    int64_t od, oh, ow;
+    if (!out_len(D, k, stride, pad, 1, &od) || !out_len(H, k, stride, pad, 1, &oh) ||
+        !out_len(W, k, stride, pad, 1, &ow) || od <= 0 || oh <= 0 || ow <= 0)
+        return fail(CONVFUSE_ERR_SHAPE,
+                    "%s: D=%lld H=%lld W=%lld k=%lld stride=%lld pad=%lld give no output", fn,
+                    (long long)D, (long long)H, (long long)W, (long long)k, (long long)stride,
+                    (long long)pad);
+    *OD = od;
+    *OH = oh;
+    *OW = ow;
+    return CONVFUSE_OK;
+}
+
+int convfuse_out_dims_conv2d(int64_t H, int64_t W, int64_t K, int64_t stride, int64_t pad,
+                             int64_t dilation, int64_t *Ho, int64_t *Wo)
+{
+    const char *fn = "convfuse_out_dims_conv2d";
+    if (!Ho || !Wo) return fail(CONVFUSE_ERR_NULL, "%s: Ho and Wo are required", fn);
+    int64_t ho, wo;
+    if (!out_len(H, K, stride, pad, dilation, &ho) || !out_len(W, K, stride, pad, dilation, &wo) ||
+        ho <= 0 || wo <= 0)
+        return fail(CONVFUSE_ERR_SHAPE,
+                    "%s: H=%lld W=%lld K=%lld stride=%lld pad=%lld dilation=%lld give no output",
+                    fn, (long long)H, (long long)W, (long long)K, (long long)stride,
+                    (long long)pad, (long long)dilation);
+    *Ho = ho;
+    *Wo = wo;
+    return CONVFUSE_OK;
+}
+
+#ifndef CONVFUSE_SOURCE_SHA
+#define CONVFUSE_SOURCE_SHA "unknown"
+#endif
+const char *convfuse_build_id(void) { return CONVFUSE_SOURCE_SHA; }
+
 // Validation and dispatch shared by conv3d_mish_tanh and its split-bf16 mode.
 static int conv3d_act_entry(const char *fn, bool split, const float *x, const float *w,
                             const float *b, float *y, int64_t N, int64_t Cin, int64_t D,

@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256 * WH, 2 / WH) void dwsep_persistent_kernel(
 // Opt-in emulation of the fp32 pointwise GEMM on bf16 matrix cores: each fp32 operand v is
 // split into hi = bf16(v) (nearest) and lo = bf16(v - hi), and v*w is taken as
 // hi_v*hi_w + hi_v*lo_w + lo_v*hi_w with fp32 accumulation (the dropped lo*lo term and the
-// split residuals are below 2^-15 of |v*w|).  The depthwise step stays fp32 on the vector
+// split residuals change each product by at most 3 * 2^-16 |v*w|).  The depthwise step stays fp32 on the vector
 // ALUs.  One 16x16x32 bf16 k-step covers a 32-channel chunk: lane group g = lane/16 holds
 // the channels g + 4i (i = 0..7) of its output channel (A) or pixel (B), so the four groups
 // read four different LDS bank groups of the halo.  Same tiles, staging, prefetch and

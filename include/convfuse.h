@@ -21,7 +21,7 @@
  *     anything is launched, so a non-OK return from validation has no side effects.
  *     convfuse_last_error() returns a message for the calling thread's last failure.
  *   - Output sizes follow floor((in + 2*pad - dilation*(k-1) - 1)/stride) + 1
- *     (convfuse_conv_out_len).
+ *     (convfuse_conv_out_len; whole shapes: convfuse_out_dims_conv3d / _conv2d).
  *   - Outputs are written only where they exist; ragged tiles never write past them.
  */
 #ifndef CONVFUSE_H
@@ -221,6 +221,33 @@ int pointwise_conv2d(const float *x, const float *pw_w, const float *pw_b, float
 int convfuse_conv_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dilation,
                           int64_t *out);
 
+/*
+ * Output sizes of the valid/padded Conv3d of conv3d_mish_tanh: OD = (D + 2*pad - k)/stride + 1,
+ * and likewise OH, OW (page "Kimi-K2.6 l2_p47", the output-size line of the generalised
+ * stride/padding kernel; 32 x 64 x 64 with k = 3 gives 30 x 62 x 62).  Pure host function, no
+ * device is touched.  Writes *OD, *OH, *OW and returns CONVFUSE_OK; CONVFUSE_ERR_NULL for a
+ * NULL output pointer; CONVFUSE_ERR_SHAPE (outputs untouched) for a non-positive size, k or
+ * stride, a negative pad, a size above 2^24, or an empty output.
+ */
+int convfuse_out_dims_conv3d(int64_t D, int64_t H, int64_t W, int64_t k, int64_t stride,
+                             int64_t pad, int64_t *OD, int64_t *OH, int64_t *OW);
+
+/*
+ * Output sizes of the depthwise step of dwsep_conv2d (and of the whole layer):
+ * Ho = (H + 2*pad - dilation*(K-1) - 1)/stride + 1, likewise Wo (page "Kimi-K2.6 l1_p86", the
+ * output-size formula; 512 x 512 at K = 3, pad 1 stays 512 x 512).  Pure host function.
+ * Writes *Ho, *Wo and returns CONVFUSE_OK; CONVFUSE_ERR_NULL for a NULL output pointer;
+ * CONVFUSE_ERR_SHAPE (outputs untouched) for a non-positive size, K, stride or dilation, a
+ * negative pad, a size above 2^24, or an empty output.
+ */
+int convfuse_out_dims_conv2d(int64_t H, int64_t W, int64_t K, int64_t stride, int64_t pad,
+                             int64_t dilation, int64_t *Ho, int64_t *Wo);
+
+/* Hash of the kernel and ABI sources this library was compiled from (16 hex digits, or
+ * "unknown" for a build that did not stamp it), so a caller can tell which sources a loaded
+ * binary was built from.  Static string. */
+const char *convfuse_build_id(void);
+
 /* Message describing the calling thread's most recent failed call ("" if none).  The
  * pointer stays valid until the thread's next failing call. */
 const char *convfuse_last_error(void);
@@ -237,8 +264,9 @@ int convfuse_measure_mfma(float *out, int64_t iters, int64_t workgroups, void *s
 
 /* ABI version (major * 100 + minor).  A caller built against this header can compare
  * CONVFUSE_ABI_VERSION with what the loaded library returns; minor versions only add entry
- * points (1.01 added the unfused steps', the split-bf16 and the diagnostic entry points). */
-#define CONVFUSE_ABI_VERSION 101
+ * points (1.01 added the unfused steps', the split-bf16 and the diagnostic entry points;
+ * 1.02 the whole-shape helpers convfuse_out_dims_conv3d / _conv2d and convfuse_build_id). */
+#define CONVFUSE_ABI_VERSION 102
 int convfuse_abi_version(void);
 
 #ifdef __cplusplus

@@ -26,3 +26,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Lines the whole-output parity tests record (count compared, largest error); printed at the
+# end of the session so they show under -q as well.
+PARITY_REPORT = []
+
+
+def pytest_terminal_summary(terminalreporter):
+    if PARITY_REPORT:
+        terminalreporter.section("whole-output parity against the fp64 oracle")
+        for line in PARITY_REPORT:
+            terminalreporter.write_line(line)

@@ -30,7 +30,66 @@ def test_library_exports_every_declared_symbol():
     L = cf.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.convfuse_abi_version() == 101
+    assert L.convfuse_abi_version() == 102
+
+
+def test_library_was_built_from_this_tree():
+    from implicit_gemm_convolution_conv3d_amd import _build
+    assert cf.build_id() == _build.source_sha()
+
+
+def _golden(key):
+    import json
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_values.json")
+    return json.load(open(path))[key]["value"]
+
+
+def test_out_dims_conv3d_page_shapes():
+    # Conv3d + Mish + Tanh: [16,32,32,64,64] with a 3^3 kernel -> [16,64,30,62,62]
+    g = _golden("conv3d_mish_tanh_output_shape")
+    assert cf.out_dims_conv3d(*g["input"][2:], 3) == tuple(g["output"][2:])
+    # the pooling workload's conv: [.,8,16,64,64] -> 14 x 62 x 62, then pool 2 -> 7 x 31 x 31
+    g = _golden("pool_conv_output_shape")
+    conv = cf.out_dims_conv3d(*g["input"][2:], 3)
+    assert conv == tuple(g["conv_output"][2:])
+    pooled = cf.out_dims_conv3d(*conv, 2, 2, 0)
+    assert pooled == tuple(_golden("pool_pooled_shape")[2:])
+    assert pooled[0] * pooled[1] * pooled[2] == _golden("pool_pooled_count")
+
+
+def test_out_dims_conv2d_page_shapes():
+    g = _golden("dwsep_output_shape")
+    assert cf.out_dims_conv2d(*g["input"][2:], 3, 1, 1, 1) == tuple(g["output"][2:])
+    assert cf.out_dims_conv2d(333, 517, 3, 1, 1, 1) == (333, 517)
+    assert cf.out_dims_conv2d(512, 512, 5, 2, 2, 1) == (256, 256)
+    assert cf.out_dims_conv2d(20, 9, 3, 1, 2, 2) == (20, 9)
+    assert cf.out_dims_conv2d(7, 7, 3, 2, 0, 1) == (3, 3)
+
+
+@pytest.mark.parametrize("args", [(0, 8, 8, 3, 1, 0), (2, 8, 8, 3, 1, 0), (8, 8, 8, 3, 0, 0),
+                                  (8, 8, 8, 3, 1, -1), (8, 8, 8, 0, 1, 0), (8, 1 << 25, 8, 3, 1, 0)])
+def test_out_dims_conv3d_rejects(args):
+    with pytest.raises(cf.ConvFuseError) as e:
+        cf.out_dims_conv3d(*args)
+    assert e.value.code == cf.ERR_SHAPE
+    assert "convfuse_out_dims_conv3d" in cf.lib().convfuse_last_error().decode()
+
+
+@pytest.mark.parametrize("args", [(8, 0, 3, 1, 1, 1), (2, 8, 5, 1, 0, 1), (8, 8, 3, 0, 1, 1),
+                                  (8, 8, 3, 1, 1, 0), (8, 8, 3, 1, -1, 1)])
+def test_out_dims_conv2d_rejects(args):
+    with pytest.raises(cf.ConvFuseError) as e:
+        cf.out_dims_conv2d(*args)
+    assert e.value.code == cf.ERR_SHAPE
+
+
+def test_out_dims_null_pointers():
+    L = cf.lib()
+    v = ctypes.c_int64(-7)
+    assert L.convfuse_out_dims_conv3d(8, 8, 8, 3, 1, 0, None, ctypes.byref(v),
+                                      ctypes.byref(v)) == cf.ERR_NULL
+    assert L.convfuse_out_dims_conv2d(8, 8, 3, 1, 1, 1, ctypes.byref(v), None) == cf.ERR_NULL
+    assert v.value == -7
 
 
 @pytest.mark.parametrize("args,expected", [

@@ -77,3 +77,29 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_matrix_work_excludes_the_depthwise_step():
+    # the pointwise GEMM alone runs on the matrix cores: 2 * pixels * Cin * Cout FLOP
+    assert bench.gemm_macs(wl.WORKLOADS[4]) == 16 * 512 * 512 * 64 * 128
+    assert bench.gemm_macs(wl.WORKLOADS[5]) == 8 * 333 * 517 * 96 * 192
+    # the Conv3d layers are one contraction
+    for i in (1, 2, 3, 6, 7, 9):
+        assert bench.gemm_macs(wl.WORKLOADS[i]) == bench.work(wl.WORKLOADS[i])[0]
+    assert bench.graded_bound(wl.WORKLOADS[4]) == bench.graded_bound(wl.WORKLOADS[5]) == "hbm"
+    assert bench.graded_bound(wl.WORKLOADS[2]) == bench.graded_bound(wl.WORKLOADS[3]) == "mfma"
+
+
+def test_workload_figures_grade_against_the_right_roof():
+    import numpy as np
+    w4 = wl.WORKLOADS[4]
+    ms = np.array([0.80, 0.70, 0.75])
+    rec = bench.workload_figures(w4, ms, ms, None)
+    assert rec["ms_median"] == 0.75
+    macs, nbytes = bench.work(w4)
+    assert rec["frac_hbm"] == round(nbytes / 0.75e-3 / 8e12, 4)
+    assert rec["frac_fp32_mfma"] == round(2 * 16 * 512 * 512 * 64 * 128 / 0.75e-3 / 157.3e12, 4)
+    assert rec["graded"]["bound"] == "hbm" and rec["graded"]["frac"] == rec["frac_hbm"]
+    rec3 = bench.workload_figures(wl.WORKLOADS[3], ms, ms, ms)
+    assert rec3["graded"]["bound"] == "mfma" and rec3["vector_gflop"] == 0
+    assert bench.workload_figures(wl.WORKLOADS[1], ms, ms, None)["graded"] is None

@@ -1,0 +1,179 @@
+"""Whole-output GPU parity at the five full-size configurations (and the pooled tensor of the
+pooling layer): every element the HIP path writes, through the C ABI, in the launch
+configuration the benchmark times, is compared with the fp64 CPU oracle on the same seeded
+inputs.  The oracle runs one batch item (or one slab of batch items) at a time, so host
+memory stays bounded.  Configurations 1 and 2 run on five seeds, as the pages' own
+correctness check ran five trials (page "Kimi-K2.6 l2_p8", its closing correctness passage).
+
+Tolerances (as stated for the hot path):
+  * conv3d_mish_tanh, dwsep_conv2d, the pooled tensor: |gpu - ref| <= 1e-4 + 1e-4 |ref|
+    elementwise;
+  * conv3d_div_maxpool_gap_bias_sum: |gpu - ref| <= 1e-4 |ref| per batch scalar.  out[n] is
+    a sum of two parts, S[n] (the mean window maxima over channels) and the bias sum B; where
+    they cancel (|S[n]| + |B| > 10 |ref|) a relative bound on ref would measure the
+    cancellation rather than the kernel, so such a scalar is judged against 1e-4 (|S[n]| + |B|)
+    and counted as conditioned in the report.
+Each test records the count compared, the largest error and the largest error-to-bound ratio;
+the session prints them at the end."""
+import numpy as np
+import pytest
+
+import oracle
+from implicit_gemm_convolution_conv3d_amd import workloads as wl
+
+from conftest import PARITY_REPORT
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-4
+POOL_RTOL = 1e-4
+SEEDS = 5  # trials for the two small-output configurations
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def cf():
+    import implicit_gemm_convolution_conv3d_amd as m
+    return m
+
+
+def dev(a):
+    if a is None:
+        return None
+    return _torch().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+class Tally:
+    """Elementwise comparison accumulated over slabs of one output."""
+
+    def __init__(self, what):
+        self.what, self.count, self.max_err, self.max_ratio = what, 0, 0.0, 0.0
+
+    def add(self, got, ref, where):
+        got = np.asarray(got, np.float64)
+        assert got.shape == ref.shape, (where, got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), "%s %s: non-finite output" % (self.what, where)
+        err = np.abs(got - ref)
+        bound = ATOL + RTOL * np.abs(ref)
+        ratio = err / bound
+        worst = int(np.argmax(ratio))
+        bad = int((err > bound).sum())
+        assert bad == 0, "%s %s: %d/%d outside tolerance; worst err %.3g at ref %.6g" % (
+            self.what, where, bad, err.size, err.reshape(-1)[worst], ref.reshape(-1)[worst])
+        self.count += err.size
+        self.max_err = max(self.max_err, float(err.max()))
+        self.max_ratio = max(self.max_ratio, float(ratio.max()))
+
+    def report(self, extra=""):
+        PARITY_REPORT.append("%-44s %12d compared  max|err| %.3e  max err/bound %.4f%s" % (
+            self.what, self.count, self.max_err, self.max_ratio, extra))
+
+
+# ----------------------------------------------------------------- configuration 1
+@pytest.mark.parametrize("trial", range(SEEDS))
+def test_config1_tiny_conv3d_mish_tanh_every_output(trial):
+    w = wl.WORKLOADS[1]
+    inp = w.inputs(w.seed + 1000 * trial)
+    ref = oracle.conv3d_mish_tanh(inp["x"], inp["w"], inp["b"])
+    y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
+    assert tuple(y.shape) == (1, 8, 6, 14, 14)
+    t = Tally("config 1 %s seed %d" % (w.name, w.seed + 1000 * trial))
+    t.add(y.cpu().numpy(), ref, "")
+    t.report()
+
+
+# ----------------------------------------------------------------- configuration 2
+def _pool_check(inp, got, what):
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"], inp["w"], inp["conv_b"], 2.0, 2,
+                                                 inp["bias"])
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape == (128,)
+    assert np.all(np.isfinite(got))
+    bsum = float(np.sum(inp["bias"].astype(np.float64)))
+    scale = np.abs(ref - bsum) + abs(bsum)          # |S[n]| + |B|
+    conditioned = scale > 10 * np.abs(ref)
+    bound = POOL_RTOL * np.where(conditioned, scale, np.abs(ref))
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), "%s: %s" % (what, [(int(i), got[i], ref[i])
+                                                     for i in np.nonzero(err > bound)[0][:8]])
+    PARITY_REPORT.append(
+        "%-44s %12d compared  max|err| %.3e  max rel err %.3e  max err/bound %.4f  "
+        "conditioned %d" % (what, got.size, err.max(), float(np.max(err / np.abs(ref))),
+                            float(np.max(err / bound)), int(conditioned.sum())))
+
+
+@pytest.mark.parametrize("trial", range(SEEDS))
+def test_config2_pool_sum_every_scalar(trial):
+    w = wl.WORKLOADS[2]
+    seed = w.seed + 1000 * trial
+    inp = w.inputs(seed)
+    out = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
+                                               2.0, 2, dev(inp["bias"]))
+    _pool_check(inp, out.cpu().numpy(), "config 2 %s seed %d" % (w.name, seed))
+
+
+# ----------------------------------------------------------------- configuration 3
+def test_config3_conv3d_mish_tanh_every_output():
+    torch = _torch()
+    w = wl.WORKLOADS[3]
+    inp = w.inputs()
+    y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
+    assert tuple(y.shape) == (16, 64, 30, 62, 62)
+    # Deterministic: a second run is bit-identical.
+    y2 = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
+    assert bool(torch.equal(y, y2))
+    del y2
+    host = y.cpu().numpy()
+    del y
+    t = Tally("config 3 %s" % w.name)
+    for n in range(host.shape[0]):
+        ref = oracle.conv3d_mish_tanh(inp["x"][n:n + 1], inp["w"], inp["b"])
+        t.add(host[n:n + 1], ref, "batch item %d" % n)
+    assert t.count == 16 * 64 * 30 * 62 * 62
+    t.report()
+
+
+# ----------------------------------------------------------------- configurations 4 and 5
+@pytest.mark.parametrize("index", [4, 5])
+def test_dwsep_every_output(index):
+    torch = _torch()
+    w = wl.WORKLOADS[index]
+    inp = w.inputs()
+    p, d = w.params, w.dims
+    args = (dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]), dev(inp["pw_b"]),
+            p["stride"], p["pad"], p["dilation"])
+    y = cf().dwsep_conv2d(*args)
+    assert tuple(y.shape) == (d["N"], d["O"], d["H"], d["W"])
+    y2 = cf().dwsep_conv2d(*args)
+    assert bool(torch.equal(y, y2))
+    del y2, args
+    host = y.cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    t = Tally("config %d %s" % (index, w.name))
+    for n in range(d["N"]):
+        ref = oracle.dwsep_conv2d(inp["x"][n:n + 1], inp["dw_w"], inp["dw_b"], inp["pw_w"],
+                                  inp["pw_b"], p["stride"], p["pad"], p["dilation"])
+        t.add(host[n:n + 1], ref, "batch item %d" % n)
+    assert t.count == d["N"] * d["O"] * d["H"] * d["W"]
+    t.report()
+
+
+# ----------------------------------------------------------------- pooled tensor
+def test_pooled_tensor_every_output():
+    """The pooling layer's shape with the pooled tensor [128,16,7,31,31] as output."""
+    w = wl.WORKLOADS[9]
+    inp = w.inputs()
+    y = cf().conv3d_div_maxpool(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]), 2.0, 2)
+    assert tuple(y.shape) == (128, 16, 7, 31, 31)
+    host = y.cpu().numpy()
+    del y
+    t = Tally("workload 9 %s" % w.name)
+    for n0 in range(0, 128, 16):
+        ref = oracle.conv3d_div_maxpool(inp["x"][n0:n0 + 16], inp["w"], inp["conv_b"], 2.0, 2)
+        t.add(host[n0:n0 + 16], ref, "batch items %d..%d" % (n0, n0 + 15))
+    assert t.count == 128 * 16 * 7 * 31 * 31
+    t.report()
