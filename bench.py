@@ -558,15 +558,20 @@ class Flusher:
 
     def __call__(self, rep):
         self.w.fill_(float(rep))
-        self.torch.sum(self.r, out=self.s)
+        self.torch.sum(self.r, dim=0, out=self.s)
 
 
 def launch_times(torch, stream, fn, reps, flush):
     """Milliseconds of `reps` launches of fn, each between two HIP events on the launch
-    stream; flush (if given) runs before each launch, outside its events."""
+    stream; flush (if given) runs before each launch, outside its events.  The same number of
+    launches (flushed alike) runs first, untimed: the first few dozen launches of a workload
+    after another one ran measure up to 15 % slower than the steady state."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
-    fn()
+    for r in range(reps):
+        if flush is not None:
+            flush(r)
+        fn()
     for r, (a, b) in enumerate(ev):
         if flush is not None:
             flush(r)
