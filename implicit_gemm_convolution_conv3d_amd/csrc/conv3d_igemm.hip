@@ -140,12 +140,15 @@ __global__ __launch_bounds__(64 * WD * WH, 2) void conv3d_mish_tanh_kernel(
     float *xs = lds;
     float *ws = lds + XS;
 
+    // Output-channel group fastest: the groups of one spatial tile are neighbouring tiles, so
+    // they run close together on one XCD and the later ones find the tile's input in its L2.
     int64_t t = xcd_tile(blockIdx.x, tiles);
+    const int ogs = (int)((d.O + 16 * MB - 1) / (16 * MB));
+    const int og = (int)(t % ogs); t /= ogs;
     const int tw = (int)(t % tiles_w); t /= tiles_w;
     const int th = (int)(t % tiles_h); t /= tiles_h;
     const int td = (int)(t % tiles_d); t /= tiles_d;
-    const int64_t n = t % d.N;
-    const int og = (int)(t / d.N);
+    const int64_t n = t;
 
     const int od0 = td * WD, oh0 = th * WH, ow0 = tw * MAIN, o0 = og * 16 * MB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
