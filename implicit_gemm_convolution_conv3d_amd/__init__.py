@@ -19,7 +19,7 @@ __all__ = [
     "conv3d_bias", "mish_tanh", "div_maxpool_gap_bias_sum", "depthwise_conv2d",
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
     "conv3d_div_maxpool_gap_bias_sum_split_bf16", "conv_out_len", "out_dims_conv3d",
-    "out_dims_conv2d", "build_id", "measure_mfma",
+    "out_dims_conv2d", "build_id", "last_kernel", "measure_mfma",
     "ConvFuseError", "lib", "library_path", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "pointwise_conv2d", "dwsep_conv2d_split_bf16", "conv3d_mish_tanh_split_bf16",
     "conv3d_div_maxpool_gap_bias_sum_split_bf16",
     "convfuse_conv_out_len", "convfuse_out_dims_conv3d", "convfuse_out_dims_conv2d",
-    "convfuse_build_id", "convfuse_last_error", "convfuse_abi_version",
+    "convfuse_build_id", "convfuse_last_kernel", "convfuse_last_error", "convfuse_abi_version",
     "convfuse_measure_mfma",
 )
 
@@ -90,6 +90,7 @@ def lib():
             L.convfuse_out_dims_conv2d.argtypes = [_i64] * 6 + [ctypes.POINTER(_i64)] * 2
             L.convfuse_measure_mfma.argtypes = [_vp, _i64, _i64, _vp]
             L.convfuse_last_error.restype = ctypes.c_char_p
+            L.convfuse_last_kernel.restype = ctypes.c_char_p
             L.convfuse_abi_version.restype = ctypes.c_int
             for name in ("conv3d_mish_tanh", "conv3d_div_maxpool_gap_bias_sum", "dwsep_conv2d",
                          "convfuse_conv_out_len"):
@@ -132,6 +133,11 @@ def out_dims_conv2d(H, W, K, stride=1, pad=0, dilation=1):
     o = [_i64() for _ in range(2)]
     _check(lib().convfuse_out_dims_conv2d(H, W, K, stride, pad, dilation, *map(ctypes.byref, o)))
     return tuple(v.value for v in o)
+
+
+def last_kernel():
+    """Name of the last kernel this thread launched through the library."""
+    return lib().convfuse_last_kernel().decode()
 
 
 def build_id():

@@ -14,6 +14,7 @@
 namespace {
 
 thread_local char g_err[512];
+thread_local const char *g_last_kernel = "";
 
 int fail(int code, const char *fmt, ...)
 {
@@ -71,9 +72,15 @@ int device_status(hipError_t e, const char *what)
 
 }  // namespace
 
+namespace convfuse {
+void note_kernel(const char *name) { g_last_kernel = name; }
+}  // namespace convfuse
+
 extern "C" {
 
 int convfuse_abi_version(void) { return CONVFUSE_ABI_VERSION; }
+
+const char *convfuse_last_kernel(void) { return g_last_kernel; }
 
 int convfuse_measure_mfma(float *out, int64_t iters, int64_t workgroups, void *stream)
 {

@@ -347,6 +347,7 @@ void launch_act_kernel(const float *x, const float *w, const float *b, float *y,
 {
     const int sw = conv_store_width(y, d.OW);
     auto go = [&](auto kern) {
+        note_kernel("conv3d_mish_tanh_kernel");
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, b, y, d,
                            tiles, (int)tw, (int)th, (int)td);
     };
@@ -376,6 +377,7 @@ void launch_pool_kernel(const float *x, const float *w, const float *conv_b, flo
                         const PoolDims &p, int64_t tiles, int64_t tw, int64_t th, int64_t td,
                         float inv_count, hipStream_t s)
 {
+    note_kernel("conv3d_pool_sum_kernel");
     hipLaunchKernelGGL((conv3d_pool_sum_kernel<MB, NBW, WD, WH, CC, VEC, BUF, BUF, STORE>),
                        dim3((unsigned)tiles), dim3(64 * WD * WH), 0, s, x, w, conv_b, out, p,
                        tiles, (int)tw, (int)th, (int)td, inv_count);
@@ -422,6 +424,7 @@ hipError_t launch_conv3d_bias(const float *x, const float *w, const float *b, fl
 hipError_t launch_pool_sum_init(const float *bias, float *out, int64_t N, int64_t O,
                                 hipStream_t s)
 {
+    note_kernel("pool_sum_init_kernel");
     hipLaunchKernelGGL(pool_sum_init_kernel, dim3((unsigned)cdiv(N, 256)), dim3(256), 0, s, bias,
                        out, N, O);
     return hipGetLastError();

@@ -324,6 +324,7 @@ hipError_t launch_split(const float *x, const float *w, const float *b, float *y
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int sw = conv_store_width(y, d.OW);
     auto go = [&](auto kern) {
+        note_kernel("conv3d_split_kernel");
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), 0, s, x, w, b, y, d, tiles,
                            (int)tw, (int)th, (int)td);
     };
@@ -347,6 +348,7 @@ hipError_t launch_pool_split(const float *x, const float *w, const float *conv_b
     const int64_t tiles = tw * th * p.PD * d.N * cdiv(d.O, 16);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    note_kernel("conv3d_pool_split_kernel");
     hipLaunchKernelGGL((conv3d_pool_split_kernel<WH, NBW, STORE>), dim3((unsigned)tiles),
                        dim3(64 * WH), 0, s, x, w, conv_b, out, p, tiles, (int)tw, (int)th,
                        inv_count);

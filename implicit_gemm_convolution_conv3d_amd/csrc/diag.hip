@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float *out, int iters)
 
 hipError_t launch_mfma_loop(float *out, int iters, int workgroups, hipStream_t s)
 {
+    note_kernel("mfma_loop_kernel");
     hipLaunchKernelGGL(mfma_loop_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, out,
                        iters);
     return hipGetLastError();

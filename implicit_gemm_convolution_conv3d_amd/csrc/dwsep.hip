@@ -798,6 +798,7 @@ hipError_t launch_persistent(const float *x, const float *dw_w, const float *dw_
     int64_t grid = (int64_t)per_cu * cu_count() / kNumXcd * kNumXcd;
     if (grid < 1) grid = 1;
     if (grid > tiles) grid = tiles;
+    note_kernel("dwsep_persistent_kernel");
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), lds, s, x, dw_w, dw_b, pw_w, pw_b,
                        y, d, obase, tiles, (int)tw, (int)th);
     return hipGetLastError();
@@ -811,6 +812,7 @@ hipError_t launch_chunked(const float *x, const float *dw_w, const float *dw_b, 
     const int64_t tw = cdiv(d.Wo, kDwTW), th = cdiv(d.Ho, R);
     const int64_t tiles = tw * th * d.N;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    note_kernel("dwsep_chunked_kernel");
     hipLaunchKernelGGL((dwsep_chunked_kernel<MB, R, VEC, DW>), dim3((unsigned)tiles),
                        dim3(256), 0, s, x, dw_w, dw_b, pw_w, pw_b, y, d, obase, tiles, (int)tw,
                        (int)th);
@@ -903,6 +905,7 @@ hipError_t launch_split_kernel(const float *x, const float *dw_w, const float *d
     int64_t grid = (int64_t)cu_count() / kNumXcd * kNumXcd;
     if (grid < 1) grid = 1;
     if (grid > tiles) grid = tiles;
+    note_kernel("dwsep_split_kernel");
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), lds, s, x, dw_w, dw_b, pw_w, pw_b,
                        y, d, obase, tiles, (int)tw, (int)th);
     return hipGetLastError();

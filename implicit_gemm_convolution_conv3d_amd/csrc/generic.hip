@@ -847,6 +847,7 @@ hipError_t launch_staged_sw(const float *x, const float *w, const float *b, floa
     const int64_t tw = cdiv(d.OW, 16 * NBW), th = cdiv(d.OH, G::WH), td = cdiv(d.OD, G::WD);
     const int64_t tiles = tw * th * td * d.N * cdiv(d.O, 16 * MB);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    note_kernel("conv3d_staged_kernel");
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), lds, s, x, w, b, y, d, tiles,
                        (int)tw, (int)th, (int)td);
     return hipGetLastError();
@@ -887,11 +888,13 @@ hipError_t launch_conv3d_generic(const float *x, const float *w, const float *b,
     if (d.O > 32) {
         const int64_t tiles = cdiv(d.O, 64) * d.N * d.OD * d.OH * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
+        note_kernel("conv3d_mish_tanh_generic_kernel");
         hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<4, NB, ACT>), dim3(grid),
                            dim3(64 * kGenWaves), 0, s, x, w, b, y, d, g, tiles, (int)tw);
     } else {
         const int64_t tiles = cdiv(d.O, 16) * d.N * d.OD * d.OH * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
+        note_kernel("conv3d_mish_tanh_generic_kernel");
         hipLaunchKernelGGL((conv3d_mish_tanh_generic_kernel<1, NB, ACT>), dim3(grid),
                            dim3(64 * kGenWaves), 0, s, x, w, b, y, d, g, tiles, (int)tw);
     }
@@ -931,6 +934,7 @@ hipError_t launch_pool_staged(const float *x, const float *w, const float *conv_
     hipError_t e = hipFuncSetAttribute((const void *)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    note_kernel("conv3d_pool_staged_kernel");
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(G::NT), lds, s, x, w, conv_b, out, p,
                        tiles, (int)tw, (int)th, inv_count);
     return hipGetLastError();
@@ -965,6 +969,7 @@ hipError_t launch_pool_generic(const float *x, const float *w, const float *conv
     unsigned grid;
     if (hipError_t e = launch_waves(tiles, grid)) return e;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    note_kernel("conv3d_pool_sum_generic_kernel");
     hipLaunchKernelGGL((conv3d_pool_sum_generic_kernel<MB, NB, STORE>), dim3(grid),
                        dim3(64 * kGenWaves), 0, s, x, w, conv_b, out, p, g, pool, tiles, (int)tw,
                        inv_count);
@@ -1004,6 +1009,7 @@ hipError_t launch_dwsep_staged_g(const float *x, const float *dw_w, const float 
     const int64_t tw = cdiv(d.Wo, 64), th = cdiv(d.Ho, R);
     const int64_t tiles = tw * th * d.N * cdiv(d.O, 16 * MB);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    note_kernel("dwsep_staged_kernel");
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, s, x, dw_w, dw_b, pw_w, pw_b,
                        y, d, geo, tiles, (int)tw, (int)th);
     return hipGetLastError();
@@ -1096,11 +1102,13 @@ hipError_t launch_dwsep_conv2d_generic(const float *x, const float *dw_w, const 
     if (d.O > 64) {
         const int64_t tiles = cdiv(d.O, 128) * d.N * d.Ho * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
+        note_kernel("dwsep_generic_kernel");
         hipLaunchKernelGGL((dwsep_generic_kernel<8>), dim3(grid), dim3(64 * kGenWaves), 0, s, x,
                            dw_w, dw_b, pw_w, pw_b, y, d, g, tiles, (int)tw);
     } else {
         const int64_t tiles = cdiv(d.O, 16) * d.N * d.Ho * tw;
         if (hipError_t e = launch_waves(tiles, grid)) return e;
+        note_kernel("dwsep_generic_kernel");
         hipLaunchKernelGGL((dwsep_generic_kernel<1>), dim3(grid), dim3(64 * kGenWaves), 0, s, x,
                            dw_w, dw_b, pw_w, pw_b, y, d, g, tiles, (int)tw);
     }

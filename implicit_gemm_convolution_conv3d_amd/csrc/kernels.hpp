@@ -6,6 +6,10 @@
 
 namespace convfuse {
 
+// Records, for the calling thread, the name of the kernel it is about to launch (a string
+// literal); convfuse_last_kernel() returns it.
+void note_kernel(const char *name);
+
 // Shape of a Conv3d with a cubic kernel; O* are the output sizes, pad the zero padding on
 // every side.  Kernel size and stride are implied (3 and 1) for the tuned kernels and given
 // by GenConv for the general ones.

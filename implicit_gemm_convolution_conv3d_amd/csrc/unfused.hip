@@ -126,6 +126,7 @@ hipError_t launch_mish_tanh(const float *v, float *y, int64_t count, hipStream_t
 {
     const bool vec = ((uintptr_t)v & 15) == 0 && ((uintptr_t)y & 15) == 0;
     const unsigned grid = stride_grid(vec ? cdiv(count, 4) : count, 256);
+    note_kernel("mish_tanh_kernel");
     if (vec)
         hipLaunchKernelGGL(mish_tanh_kernel<true>, dim3(grid), dim3(256), 0, s, v, y, count);
     else
@@ -142,6 +143,7 @@ hipError_t launch_div_maxpool_gap_bias_sum(const float *conv, const float *bias,
     const int64_t blocks = d.N * d.O;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float inv_count = (float)(1.0 / ((double)p.PD * (double)p.PH * (double)p.PW));
+    note_kernel("pool_reduce_kernel");
     hipLaunchKernelGGL(pool_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, conv, out, p,
                        pool, inv_count);
     return hipGetLastError();
@@ -152,6 +154,7 @@ hipError_t launch_depthwise_conv2d(const float *x, const float *dw_w, const floa
 {
     const int64_t total = d.N * d.C * d.Ho * ((d.Wo + 3) / 4);
     const unsigned grid = stride_grid(total, 256);
+    note_kernel("depthwise_kernel");
     if (d.Wo % 4 == 0 && ((uintptr_t)y & 15) == 0)
         hipLaunchKernelGGL(depthwise_kernel<true>, dim3(grid), dim3(256), 0, s, x, dw_w, dw_b, y,
                            d, g);

@@ -243,6 +243,11 @@ int convfuse_out_dims_conv3d(int64_t D, int64_t H, int64_t W, int64_t k, int64_t
 int convfuse_out_dims_conv2d(int64_t H, int64_t W, int64_t K, int64_t stride, int64_t pad,
                              int64_t dilation, int64_t *Ho, int64_t *Wo);
 
+/* Name of the last kernel the calling thread launched through the library (the main kernel
+ * of its last successful launching call, e.g. "dwsep_persistent_kernel"; "" before any), so a
+ * caller or a benchmark can see which kernel the dispatch chose.  Static string. */
+const char *convfuse_last_kernel(void);
+
 /* Hash of the kernel and ABI sources this library was compiled from (16 hex digits, or
  * "unknown" for a build that did not stamp it), so a caller can tell which sources a loaded
  * binary was built from.  Static string. */
@@ -265,7 +270,8 @@ int convfuse_measure_mfma(float *out, int64_t iters, int64_t workgroups, void *s
 /* ABI version (major * 100 + minor).  A caller built against this header can compare
  * CONVFUSE_ABI_VERSION with what the loaded library returns; minor versions only add entry
  * points (1.01 added the unfused steps', the split-bf16 and the diagnostic entry points;
- * 1.02 the whole-shape helpers convfuse_out_dims_conv3d / _conv2d and convfuse_build_id). */
+ * 1.02 the whole-shape helpers convfuse_out_dims_conv3d / _conv2d, convfuse_build_id and
+ * convfuse_last_kernel). */
 #define CONVFUSE_ABI_VERSION 102
 int convfuse_abi_version(void);
 

@@ -22,6 +22,7 @@ import oracle
 from implicit_gemm_convolution_conv3d_amd import workloads as wl
 
 from conftest import PARITY_REPORT
+import bench
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +80,7 @@ def test_config1_tiny_conv3d_mish_tanh_every_output(trial):
     inp = w.inputs(w.seed + 1000 * trial)
     ref = oracle.conv3d_mish_tanh(inp["x"], inp["w"], inp["b"])
     y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
+    assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (1, 8, 6, 14, 14)
     t = Tally("config 1 %s seed %d" % (w.name, w.seed + 1000 * trial))
     t.add(y.cpu().numpy(), ref, "")
@@ -112,6 +114,7 @@ def test_config2_pool_sum_every_scalar(trial):
     inp = w.inputs(seed)
     out = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
                                                2.0, 2, dev(inp["bias"]))
+    assert cf().last_kernel() == bench.kernel_name(w)
     _pool_check(inp, out.cpu().numpy(), "config 2 %s seed %d" % (w.name, seed))
 
 
@@ -121,6 +124,7 @@ def test_config3_conv3d_mish_tanh_every_output():
     w = wl.WORKLOADS[3]
     inp = w.inputs()
     y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
+    assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (16, 64, 30, 62, 62)
     # Deterministic: a second run is bit-identical.
     y2 = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]))
@@ -146,6 +150,7 @@ def test_dwsep_every_output(index):
     args = (dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]), dev(inp["pw_b"]),
             p["stride"], p["pad"], p["dilation"])
     y = cf().dwsep_conv2d(*args)
+    assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (d["N"], d["O"], d["H"], d["W"])
     y2 = cf().dwsep_conv2d(*args)
     assert bool(torch.equal(y, y2))
@@ -168,6 +173,7 @@ def test_pooled_tensor_every_output():
     w = wl.WORKLOADS[9]
     inp = w.inputs()
     y = cf().conv3d_div_maxpool(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]), 2.0, 2)
+    assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (128, 16, 7, 31, 31)
     host = y.cpu().numpy()
     del y

@@ -8,6 +8,7 @@ dilation > 1), so the general kernels are the ones that run."""
 import numpy as np
 import pytest
 
+import bench
 import oracle
 from implicit_gemm_convolution_conv3d_amd import workloads as wl
 
@@ -140,26 +141,29 @@ def test_general_workload_sampled(index):
     if w.op == "conv3d_mish_tanh":
         y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), p["stride"],
                                   p["pad"])
+        assert cf().last_kernel() == bench.kernel_name(w)
         idx = edge_indices(y.shape, rng, 8000)
         ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
     else:
         y = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
                               dev(inp["pw_b"]), p["stride"], p["pad"], p["dilation"])
+        assert cf().last_kernel() == bench.kernel_name(w)
         idx = edge_indices(y.shape, rng, 8000)
         ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"],
                                      inp["pw_b"], idx, p["stride"], p["pad"], p["dilation"])
     assert_close(gather(y, idx), ref, "workload %d sampled" % index)
 
 
-def test_general_pool_workload_picks():
+def test_general_pool_workload_every_scalar():
+    """The 3x3x3-pool workload at the size bench.py times it: all 128 scalars."""
     w = wl.WORKLOADS[7]
     inp = w.inputs()
     p = w.params
     out = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
                                                p["divisor"], p["pool"], dev(inp["bias"]))
+    assert cf().last_kernel() == bench.kernel_name(w)
     got = out.cpu().numpy().astype(np.float64)
-    picks = [0, 77, 127]
-    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"][picks], inp["w"], inp["conv_b"],
-                                                 p["divisor"], p["pool"], inp["bias"])
-    rel = np.abs(got[picks] - ref) / np.abs(ref)
-    assert rel.max() <= POOL_RTOL, (got[picks], ref)
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"], inp["w"], inp["conv_b"], p["divisor"],
+                                                 p["pool"], inp["bias"])
+    rel = np.abs(got - ref) / np.abs(ref)
+    assert rel.max() <= POOL_RTOL, (got, ref)

@@ -16,6 +16,7 @@ that fixes which of the split's product terms are present."""
 import numpy as np
 import pytest
 
+import bench
 import oracle
 from implicit_gemm_convolution_conv3d_amd import workloads as wl
 
@@ -118,6 +119,7 @@ def test_split_full_workload_sampled(index):
     args = (p["stride"], p["pad"], p["dilation"])
     y = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
                                      dev(inp["pw_w"]), dev(inp["pw_b"]), *args)
+    assert cf().last_kernel() == bench.kernel_name(w)
     dd = w.dims
     assert tuple(y.shape) == (dd["N"], dd["O"], dd["H"], dd["W"])
     rng = np.random.default_rng(31 + index)
@@ -197,6 +199,7 @@ def test_conv3d_split_full_workload_sampled():
     p = w.params
     y = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
                                          p["stride"], p["pad"])
+    assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (16, 64, 30, 62, 62)
     idx = edge_indices(y.shape, np.random.default_rng(41), 6000)
     ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
@@ -256,6 +259,7 @@ def test_pool_split_full_workload_picks():
     out = cf().conv3d_div_maxpool_gap_bias_sum_split_bf16(dev(inp["x"]), dev(inp["w"]),
                                                           dev(inp["conv_b"]), p["divisor"],
                                                           p["pool"], dev(inp["bias"]))
+    assert cf().last_kernel() == bench.kernel_name(w)
     got = out.cpu().numpy().astype(np.float64)
     picks = [0, 77, 127]
     sub = dict(inp, x=inp["x"][picks])
