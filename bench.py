@@ -64,12 +64,15 @@ def work(w):
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3
                       + d["O"] + outs)
     elif w.op.startswith("conv3d_div_maxpool"):
-        k = p["k"]
+        k, pool = p["k"], p["pool"]
         od, oh, ow = out_dims(w)
-        macs = d["N"] * d["O"] * od * oh * ow * d["C"] * k ** 3
+        pooled = [(s - pool) // pool + 1 for s in (od, oh, ow)]
+        # only the conv outputs some window reads: floor-mode pooling never reads the rest
+        # (none for a 2x2x2 pool on even sizes)
+        used = d["N"] * d["O"] * pool ** 3 * pooled[0] * pooled[1] * pooled[2]
+        macs = used * d["C"] * k ** 3
         nbytes = 4 * (d["N"] * d["C"] * d["D"] * d["H"] * d["W"] + d["O"] * d["C"] * k ** 3)
         if w.op == "conv3d_div_maxpool":
-            pooled = [(s - p["pool"]) // p["pool"] + 1 for s in (od, oh, ow)]
             nbytes += 4 * (d["O"] + d["N"] * d["O"] * pooled[0] * pooled[1] * pooled[2])
         else:
             nbytes += 4 * (2 * d["O"] + d["N"])

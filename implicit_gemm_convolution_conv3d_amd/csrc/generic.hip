@@ -294,11 +294,11 @@ struct PoolGeom {
     static constexpr int RS = round_up(COLS, 4);
     static constexpr int CS = halo_channel_stride(P * HHR * RS);
     static constexpr int XS = 4 * CS;
-    static constexpr int ROWS = 4 * P * HHR;                 // staged rows per chunk
     static constexpr int WSZ = K * K * 64;                   // weights per chunk (16 outputs)
     static constexpr int BUF = XS + WSZ;                     // one stage
     static constexpr int RED = 16 * (16 * NBW + 1);          // per-wave window buffer
-    static constexpr int LDS = 2 * BUF + 4 * RED;            // floats
+    // (the window buffers reuse the stages once the K loop is over)
+    static constexpr int LDS = 2 * BUF > 4 * RED ? 2 * BUF : 4 * RED;  // floats
     static_assert(COLS <= 64, "one load per staged row");
 };
 
@@ -313,7 +313,6 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
     // (the wave index made explicitly uniform: the row copy's per-row decomposition and
     // offsets are then scalar work)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    float *red = dyn + 2 * G::BUF + wave * G::RED;
     const Conv3dDims &d = p.conv;
     const int D = (int)d.D, H = (int)d.H, W = (int)d.W;
 
@@ -327,27 +326,39 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
     const int xlane = (lane >> 4) * G::CS + wave * P * G::RS + (lane & 15);
     const int id0 = P * pd0, ih0 = P * ph0, iw0 = P * pw0;
 
-    // Issue chunk q's input rows into buffer xsb: row r = channel r / (P*HHR), plane
-    // (r / HHR) % P, row r % HHR; LDS column c holds input column iw0 + c.  Byte offsets over
-    // the chunk's four channels of image n stay below 2^31 (host check).
+    // Issue chunk q's input rows into buffer xsb: wave w copies the P*HHR rows of channel
+    // c0 + w (plane pl, row hr at LDS row pl*HHR + hr); LDS column c holds input column
+    // iw0 + c.  Each plane is read through a resource that starts at its row ih0 and ends
+    // with the plane (no records for an absent channel or plane), so rows past H read as
+    // zero by the range check; lanes past W carry a dropped offset.  The loops are unrolled:
+    // a row costs an offset add and the load.
+    const int lcol = iw0 + lane < W ? 4 * lane : kDropOffset;
     auto rows_dma = [&](int q, float *xsb) {
         const int c0 = (q / K) * 4, kd = q % K;
-        const __amdgpu_buffer_rsrc_t rs =
-            buffer_rsrc(x + (n * d.C + c0) * (int64_t)D * H * W);
-        const int iw = iw0 + lane;
-        const bool colok = lane < G::COLS && iw < W;
-        for (int r = wave; r < G::ROWS; r += 4) {
-            const int cl = r / (P * G::HHR), rem = r - cl * (P * G::HHR);
-            const int pl = rem / G::HHR, hr = rem - pl * G::HHR;
-            const int id = id0 + pl + kd, ih = ih0 + hr;
-            const bool ok = colok && c0 + cl < d.C && id < D && ih < H;
-            const int off = ok ? 4 * (((cl * D + id) * H + ih) * W + iw) : kDropOffset;
-            if (lane < G::COLS)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs,
-                    (__attribute__((address_space(3))) void *)(xsb + cl * G::CS +
-                                                               (pl * G::HHR + hr) * G::RS),
-                    4, off, 0, 0, 0);
+        const int cw = c0 + wave;
+        float *dst = xsb + wave * G::CS;
+        int rstep = 4 * W;
+        asm volatile("" : "+s"(rstep));
+        if (lane < G::COLS) {
+#pragma unroll
+            for (int pl = 0; pl < P; ++pl) {
+                const int id = id0 + pl + kd;
+                const bool plok = cw < d.C && id < D;
+                const float *pbase = x + (((n * d.C + cw) * D + id) * H + ih0) * (int64_t)W + iw0;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(pbase), (short)0, plok ? 4 * (H - ih0) * W : 0,
+                    kBufferWord3);
+                int off = lcol;
+#pragma unroll
+                for (int hr = 0; hr < G::HHR; ++hr) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rs,
+                        (__attribute__((address_space(3))) void *)(dst +
+                                                                   (pl * G::HHR + hr) * G::RS),
+                        4, off, 0, 0, 0);
+                    off += rstep;
+                }
+            }
         }
     };
     WeightChunk<1, 4, G::NT, K * K> wts;
@@ -396,6 +407,9 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
         __syncthreads();                // ... and every wave's; nobody reads this stage
     }
     if (!active) return;  // (no barrier follows)
+    // Every wave is past the last barrier: no wave reads a stage and no load into one is in
+    // flight, so the stages hold the per-wave window buffers now.
+    float *red = dyn + wave * G::RED;
     // lane holds columns 4*(lane/16) + r of every block of output channel o0 + lane%16
     const bool use_min = p.divisor < 0.0f;
     const int j = lane & 15, g4 = 4 * (lane >> 4);

@@ -24,6 +24,14 @@ def test_pool_macs_match_the_page():
     assert nbytes == 4 * (128 * 8 * 16 * 64 * 64 + 16 * 8 * 27 + 16 + 16 + 128)
 
 
+def test_pool_macs_count_only_the_windows_conv_outputs():
+    # 3x3x3 pool over a 14x62x62 conv output: floor mode reads 12x60x60 of it
+    macs, _ = bench.work(wl.WORKLOADS[7])
+    assert macs == 128 * 16 * (12 * 60 * 60) * 8 * 27
+    # 2x2x2 pool on even sizes reads every conv output: the page's count
+    assert bench.work(wl.WORKLOADS[9])[0] == PAGES["pool_conv_macs"]["value"]
+
+
 def test_conv3d_macs_match_the_page():
     macs, nbytes = bench.work(wl.WORKLOADS[3])
     assert macs == (PAGES["conv3d_mish_tanh_output_elements"]["value"]
