@@ -310,8 +310,8 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
 {
     using G = PoolGeom<K, P, NBW>;
     extern __shared__ __attribute__((aligned(16))) float dyn[];
-    // (the wave index made explicitly uniform: the row copy's per-row decomposition and
-    // offsets are then scalar work)
+    // (the wave index made explicitly uniform: the row copy's channel, buffer resources and
+    // LDS addresses are then scalar work)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Conv3dDims &d = p.conv;
     const int D = (int)d.D, H = (int)d.H, W = (int)d.W;
@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
     // iw0 + c.  Each plane is read through a resource that starts at its row ih0 and ends
     // with the plane (no records for an absent channel or plane), so rows past H read as
     // zero by the range check; lanes past W carry a dropped offset.  The loops are unrolled:
-    // a row costs an offset add and the load.
+    // a row costs an offset add and the load.  A plane's byte size is below 2^31 (the host
+    // checks four channels' volume).
     const int lcol = iw0 + lane < W ? 4 * lane : kDropOffset;
     auto rows_dma = [&](int q, float *xsb) {
         const int c0 = (q / K) * 4, kd = q % K;
