@@ -345,7 +345,9 @@ __global__ __launch_bounds__(256, 2) void conv3d_pool_staged_kernel(
             for (int pl = 0; pl < P; ++pl) {
                 const int id = id0 + pl + kd;
                 const bool plok = cw < d.C && id < D;
-                const float *pbase = x + (((n * d.C + cw) * D + id) * H + ih0) * (int64_t)W + iw0;
+                // (an absent plane keeps the tensor's base: its resource has no records)
+                const float *pbase =
+                    plok ? x + (((n * d.C + cw) * D + id) * H + ih0) * (int64_t)W + iw0 : x;
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<float *>(pbase), (short)0, plok ? 4 * (H - ih0) * W : 0,
                     kBufferWord3);
