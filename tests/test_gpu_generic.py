@@ -12,6 +12,7 @@ import bench
 import oracle
 from implicit_gemm_convolution_conv3d_amd import workloads as wl
 
+from test_gpu_full_parity import Tally, _torch
 from test_gpu_parity import assert_close, cf, dev, edge_indices, gather, POOL_RTOL
 
 pytestmark = pytest.mark.gpu
@@ -132,26 +133,33 @@ def test_dwsep_general_larger_sampled():
 
 
 @pytest.mark.parametrize("index", [6, 8])
-def test_general_workload_sampled(index):
-    """The general-parameter workloads at the size bench.py times them: sampled outputs."""
+def test_general_workload_every_output(index):
+    """The general-parameter workloads at the size bench.py times them: every output, compared
+    one batch item at a time."""
+    torch = _torch()
     w = wl.WORKLOADS[index]
     inp = w.inputs()
     p = w.params
-    rng = np.random.default_rng(20 + index)
     if w.op == "conv3d_mish_tanh":
         y = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), p["stride"],
                                   p["pad"])
-        assert cf().last_kernel() == bench.kernel_name(w)
-        idx = edge_indices(y.shape, rng, 8000)
-        ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
+        ref_of = lambda n: oracle.conv3d_mish_tanh(inp["x"][n:n + 1], inp["w"], inp["b"],
+                                                   p["stride"], p["pad"])
     else:
         y = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
                               dev(inp["pw_b"]), p["stride"], p["pad"], p["dilation"])
-        assert cf().last_kernel() == bench.kernel_name(w)
-        idx = edge_indices(y.shape, rng, 8000)
-        ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"],
-                                     inp["pw_b"], idx, p["stride"], p["pad"], p["dilation"])
-    assert_close(gather(y, idx), ref, "workload %d sampled" % index)
+        ref_of = lambda n: oracle.dwsep_conv2d(inp["x"][n:n + 1], inp["dw_w"], inp["dw_b"],
+                                               inp["pw_w"], inp["pw_b"], p["stride"], p["pad"],
+                                               p["dilation"])
+    assert cf().last_kernel() == bench.kernel_name(w)
+    host = y.cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    t = Tally("workload %d %s" % (index, w.name))
+    for n in range(host.shape[0]):
+        t.add(host[n:n + 1], ref_of(n), "batch item %d" % n)
+    assert t.count == host.size
+    t.report()
 
 
 def test_general_pool_workload_every_scalar():
