@@ -11,7 +11,7 @@ output at the pixel, is
 product loses at most 3 * 2^-16 |v*w|).  The sum is computed here from the oracle's depthwise
 output (the oracle's depthwise-separable conv with an identity pointwise step).  Cases cover
 ragged tiles, channel counts off the k-steps and chunks, several output-channel slices, every
-padding the split kernels take, the full-size workloads on sampled outputs, and a closed form
+padding the split kernels take, every output of the full-size workloads, and a closed form
 that fixes which of the split's product terms are present."""
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ import bench
 import oracle
 from implicit_gemm_convolution_conv3d_amd import workloads as wl
 
-from test_gpu_parity import _torch, cf, dev, edge_indices, gather
+from conftest import PARITY_REPORT
+from test_gpu_parity import _torch, cf, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -111,8 +112,31 @@ def test_split_terms_closed_form():
     assert float((y32 - exact).abs().max()) <= 1e-4 + 1e-4 * exact
 
 
+class SplitTally:
+    """Whole-output comparison against a split contract, accumulated over batch items."""
+
+    def __init__(self, what):
+        self.what, self.count, self.max_ratio = what, 0, 0.0
+
+    def add(self, got, ref, abs_term, where):
+        got = np.asarray(got, np.float64)
+        assert got.shape == ref.shape == abs_term.shape, (where, got.shape, ref.shape)
+        assert_split_close(got, ref, abs_term, "%s %s" % (self.what, where))
+        bound = 1e-4 + 1e-4 * np.abs(ref) + SPLIT_SLACK * abs_term
+        self.count += got.size
+        self.max_ratio = max(self.max_ratio, float((np.abs(got - ref) / bound).max()))
+
+    def report(self):
+        PARITY_REPORT.append("%-44s %12d compared  max err/bound %.4f (split contract)" % (
+            self.what, self.count, self.max_ratio))
+
+
 @pytest.mark.parametrize("index", [10, 11])
-def test_split_full_workload_sampled(index):
+def test_split_full_workload_every_output(index):
+    """The dwsep split workloads at full size: every output against the split contract, one
+    batch item at a time; the sum of |d[c] * pw[o,c]| comes from the oracle's depthwise
+    output of the item."""
+    torch = _torch()
     w = wl.WORKLOADS[index]
     inp = w.inputs()
     p = w.params
@@ -122,31 +146,30 @@ def test_split_full_workload_sampled(index):
     assert cf().last_kernel() == bench.kernel_name(w)
     dd = w.dims
     assert tuple(y.shape) == (dd["N"], dd["O"], dd["H"], dd["W"])
-    rng = np.random.default_rng(31 + index)
-    idx = edge_indices(y.shape, rng, 6000)
-    ref = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
-                                 idx, *args)
-    # depthwise outputs of every channel at the sampled pixels
-    n, o, h, ww = np.unravel_index(idx, y.shape)
-    C = dd["C"]
-    cs = np.arange(C)
-    didx = np.ravel_multi_index((np.repeat(n, C), np.tile(cs, idx.size), np.repeat(h, C),
-                                 np.repeat(ww, C)), (dd["N"], C, dd["H"], dd["W"]))
-    eye = np.eye(C, dtype=np.float32).reshape(C, C, 1, 1)
-    d = oracle.dwsep_conv2d_at(inp["x"], inp["dw_w"], inp["dw_b"], eye, None, didx,
-                               *args).reshape(idx.size, C)
-    pw = np.abs(inp["pw_w"][:, :, 0, 0].astype(np.float64))
-    abs_dot = np.einsum("sc,sc->s", pw[o], np.abs(d))
-    assert_split_close(gather(y, idx), ref, abs_dot, "split workload %d sampled" % index)
-    torch = _torch()
     assert bool(torch.isfinite(y).all())
     # the split kernel ran (its rounding differs from the fp32 kernel's) and is deterministic
     y32 = cf().dwsep_conv2d(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]), dev(inp["pw_w"]),
                             dev(inp["pw_b"]), *args)
     assert not bool(torch.equal(y, y32))
+    del y32
     y2 = cf().dwsep_conv2d_split_bf16(dev(inp["x"]), dev(inp["dw_w"]), dev(inp["dw_b"]),
                                       dev(inp["pw_w"]), dev(inp["pw_b"]), *args)
     assert bool(torch.equal(y, y2))
+    del y2
+    host = y.cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    pw = np.abs(inp["pw_w"][:, :, 0, 0].astype(np.float64))
+    t = SplitTally("split workload %d %s" % (index, w.name))
+    for n in range(dd["N"]):
+        item = dict(inp, x=inp["x"][n:n + 1])
+        ref = oracle.dwsep_conv2d(item["x"], inp["dw_w"], inp["dw_b"], inp["pw_w"], inp["pw_b"],
+                                  *args)
+        d = np.abs(depthwise_exact(item, *args)[0]).reshape(dd["C"], -1)
+        abs_dot = (pw @ d).reshape(ref.shape)
+        t.add(host[n:n + 1], ref, abs_dot, "batch item %d" % n)
+    assert t.count == host.size
+    t.report()
 
 
 def test_split_not_written_past_end():
@@ -193,7 +216,10 @@ def test_conv3d_split_general_parameters_run_fp32():
     assert np.all(np.abs(got - ref) <= 1e-4 + 1e-4 * np.abs(ref))
 
 
-def test_conv3d_split_full_workload_sampled():
+def test_conv3d_split_full_workload_every_output():
+    """The Conv3d split workload at full size: every output against the split contract, one
+    batch item at a time; sum |x * w| is the oracle's Conv3d of |x| and |w| for the item."""
+    torch = _torch()
     w = wl.WORKLOADS[12]
     inp = w.inputs()
     p = w.params
@@ -201,25 +227,26 @@ def test_conv3d_split_full_workload_sampled():
                                          p["stride"], p["pad"])
     assert cf().last_kernel() == bench.kernel_name(w)
     assert tuple(y.shape) == (16, 64, 30, 62, 62)
-    idx = edge_indices(y.shape, np.random.default_rng(41), 6000)
-    ref = oracle.conv3d_mish_tanh_at(inp["x"], inp["w"], inp["b"], idx, p["stride"], p["pad"])
-    # sum |x * w| at the sampled outputs: the oracle's Conv3d of |x| and |w| over the images
-    # the samples touch
-    n_idx = np.unravel_index(idx, y.shape)[0]
-    extra = np.empty(idx.size)
-    for n in np.unique(n_idx):
-        sel = n_idx == n
-        full = oracle.conv3d(np.abs(inp["x"][n:n + 1]), np.abs(inp["w"]), None, 1, 0)
-        extra[sel] = full.reshape(-1)[idx[sel] - n * full.size]
-    assert_split_close(gather(y, idx), ref, (2.0 ** -13 / SPLIT_SLACK) * extra,
-                       "conv3d split workload sampled")
-    torch = _torch()
     assert bool(torch.isfinite(y).all())
     y32 = cf().conv3d_mish_tanh(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), p["stride"], p["pad"])
     assert not bool(torch.equal(y, y32))
+    del y32
     y2 = cf().conv3d_mish_tanh_split_bf16(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
                                           p["stride"], p["pad"])
     assert bool(torch.equal(y, y2))
+    del y2
+    host = y.cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    aw = np.abs(inp["w"])
+    t = SplitTally("split workload 12 %s" % w.name)
+    for n in range(host.shape[0]):
+        xn = inp["x"][n:n + 1]
+        ref = oracle.conv3d_mish_tanh(xn, inp["w"], inp["b"], p["stride"], p["pad"])
+        extra = oracle.conv3d(np.abs(xn), aw, None, p["stride"], p["pad"])
+        t.add(host[n:n + 1], ref, (2.0 ** -13 / SPLIT_SLACK) * extra, "batch item %d" % n)
+    assert t.count == host.size
+    t.report()
 
 
 POOL_SPLIT_CASES = [
@@ -252,7 +279,8 @@ def test_pool_split_small(case):
     assert np.all(np.abs(got - ref) <= bound), (case, got, ref, bound)
 
 
-def test_pool_split_full_workload_picks():
+def test_pool_split_full_workload_every_scalar():
+    """The pooled-sum split workload at full size: all 128 scalars against the split bound."""
     w = wl.WORKLOADS[13]
     inp = w.inputs()
     p = w.params
@@ -261,12 +289,14 @@ def test_pool_split_full_workload_picks():
                                                           p["pool"], dev(inp["bias"]))
     assert cf().last_kernel() == bench.kernel_name(w)
     got = out.cpu().numpy().astype(np.float64)
-    picks = [0, 77, 127]
-    sub = dict(inp, x=inp["x"][picks])
-    ref = oracle.conv3d_div_maxpool_gap_bias_sum(sub["x"], inp["w"], inp["conv_b"],
+    ref = oracle.conv3d_div_maxpool_gap_bias_sum(inp["x"], inp["w"], inp["conv_b"],
                                                  p["divisor"], p["pool"], inp["bias"])
-    bound = pool_split_bound(sub, ref, p["divisor"])
-    assert np.all(np.abs(got[picks] - ref) <= bound), (got[picks], ref, bound)
+    bound = pool_split_bound(inp, ref, p["divisor"])
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), [(int(i), got[i], ref[i], bound[i])
+                                  for i in np.nonzero(err > bound)[0][:8]]
+    PARITY_REPORT.append("%-44s %12d compared  max err/bound %.4f (split contract)" % (
+        "split workload 13 %s" % w.name, got.size, float((err / bound).max())))
     torch = _torch()
     assert bool(torch.isfinite(out).all())
     out32 = cf().conv3d_div_maxpool_gap_bias_sum(dev(inp["x"]), dev(inp["w"]), dev(inp["conv_b"]),
